@@ -1,0 +1,113 @@
+"""Seeded synthetic inputs for the q6_K x q8 decode GEMV.
+
+This module is shared by the oracle-side tests and the HIP-side tests and
+benchmark. It holds none of the method's arithmetic: it draws random bytes and
+random floats in the shapes and distributions of the workloads and places them
+at the byte positions of a GGUF q6_K super-block (128 B low bits, 64 B high
+bits, 16 int8 sub-block scales, fp16 super-block scale at byte 208), nothing
+more. Uniform random low/high bit bytes give codes uniform in 0..63.
+
+The super-block scale is drawn as fp16(|N(0,1)| * 1e-3) rather than random bit
+patterns, so no NaN or inf can appear (random fp16 bits make NaN != NaN
+comparisons look like differences; D4-4 §3.3, "The NaN trap").
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+BLOCK_BYTES = 210          # one q6_K super-block of 256 weights
+QL_BYTES, QH_BYTES, SC_BYTES = 128, 64, 16
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    index: int             # 1-based workload number, used in the seeds
+    name: str
+    N: int                 # output rows
+    K: int                 # input features (multiple of 256)
+    nt: tuple              # token columns exercised
+    act: str               # "normal" | "outlier" | "swiglu"
+    producer: str          # "quant" (standalone q8) | "rmsnorm" (fused RMSNorm -> q8)
+
+    @property
+    def nbe(self) -> int:
+        return self.K // 256
+
+    @property
+    def content_bytes(self) -> int:
+        return self.N * self.nbe * BLOCK_BYTES
+
+
+WORKLOADS = {
+    "tiny": Workload(1, "tiny", 64, 1024, (1,), "normal", "quant"),
+    "attn_v": Workload(2, "attn_v", 1024, 5120, (1,), "outlier", "rmsnorm"),
+    "ffn_down": Workload(3, "ffn_down", 5120, 13824, (1,), "swiglu", "quant"),
+    "tall_k": Workload(4, "tall_k", 3584, 18944, (1,), "swiglu", "quant"),
+    "lm_head": Workload(5, "lm_head", 152064, 5120, (1, 4), "outlier", "rmsnorm"),
+}
+
+RMS_EPS = 1e-6
+
+
+def weight_seed(w: Workload) -> int:
+    return 1000 * w.index
+
+
+def act_seed(w: Workload, column: int) -> int:
+    return 1000 * w.index + 1 + column
+
+
+def gamma_seed(w: Workload) -> int:
+    return 1000 * w.index + 999
+
+
+def raw_q6k(N: int, K: int, seed: int) -> np.ndarray:
+    """Random raw GGUF q6_K rows, uint8 [N, (K/256)*210]."""
+    assert K > 0 and K % 256 == 0 and N >= 0
+    nbe = K // 256
+    rng = np.random.default_rng(seed)
+    out = np.empty((N, nbe, BLOCK_BYTES), np.uint8)
+    out[:, :, :QL_BYTES + QH_BYTES] = rng.integers(
+        0, 256, size=(N, nbe, QL_BYTES + QH_BYTES), dtype=np.uint8)
+    sc = rng.integers(-32, 32, size=(N, nbe, SC_BYTES), dtype=np.int8)
+    out[:, :, 192:208] = sc.view(np.uint8)
+    d = (np.abs(rng.standard_normal((N, nbe))) * 1e-3).astype(np.float16)
+    out[:, :, 208:210] = d.view(np.uint8).reshape(N, nbe, 2)
+    return out.reshape(N, nbe * BLOCK_BYTES)
+
+
+def activation(kind: str, K: int, seed: int) -> np.ndarray:
+    """One float32 activation row of length K."""
+    rng = np.random.default_rng(seed)
+    if kind == "normal":
+        return rng.standard_normal(K, dtype=np.float32)
+    if kind == "outlier":
+        x = rng.standard_normal(K, dtype=np.float32)
+        n_out = math.ceil(0.001 * K)
+        idx = rng.choice(K, size=n_out, replace=False)
+        x[idx] *= np.float32(50.0)
+        return x
+    if kind == "swiglu":
+        g = rng.standard_normal(K, dtype=np.float32)
+        u = rng.standard_normal(K, dtype=np.float32)
+        one = np.float32(1.0)
+        return ((g / (one + np.exp(-g))) * u).astype(np.float32)
+    raise ValueError(kind)
+
+
+def activations(w: Workload, nt: int) -> np.ndarray:
+    """float32 [nt, K]; column c is drawn from its own seed."""
+    return np.stack([activation(w.act, w.K, act_seed(w, c)) for c in range(nt)])
+
+
+def gamma(K: int, seed: int) -> np.ndarray:
+    """RMSNorm weight, float32 U[0.5, 1.5]."""
+    rng = np.random.default_rng(seed)
+    return rng.uniform(0.5, 1.5, size=K).astype(np.float32)
+
+
+def weights(w: Workload) -> np.ndarray:
+    return raw_q6k(w.N, w.K, weight_seed(w))
