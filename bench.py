@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of the q6_K x q8 decode GEMV path on one MI355X.
+
+A step is one pass of the hot path over one batch: the fused RMSNorm -> q8
+producer on the activation row(s), then the q6_K (dpl) x q8 GEMV over the
+152064 x 5120 lm_head matrix (638.67 MB of q6_K content). Inputs are resident in
+HBM before timing starts. The weights rotate over enough device copies (>= 1 GiB
+in total) that the 256 MB last-level cache cannot serve them from one step to the
+next.
+
+Prints one JSON line: content GB/s of the whole step (`value`), the GEMV kernel's
+own rate against the 8 TB/s HBM peak (`roofline`, timed with HIP events on the
+stream the kernels run on), and the oracle timed on host cores (`cpu_baseline`).
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--nt 1] [--no-cpu-baseline]
+    python bench.py --copy-calib    # plain device copy of known size, for counter scaling
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+PAGES_LM_HEAD_GBS = 250.0       # the pages' dpl lm_head content rate (GB10; context only)
+ROTATE_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mmvq_lm_head_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "quantized_decode_gemv_amd", "csrc", f)
+                  for f in ("mmvq.hip", "q6k_unit.h")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(nt: int):
+    """HBM bytes per GEMV launch from the committed counter summary, or None when
+    the summary is absent or was taken on a different kernel source."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                parts = line.split()
+                if len(parts) == 2 and not line.startswith("#"):
+                    kv[parts[0]] = parts[1]
+        if kv.get("kernel_sha") != kernel_hash():
+            return None
+        return float(kv[f"bytes_per_launch_nt{nt}"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_calib(steps: int) -> None:
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calib_bytes_read": n, "copy_calib_bytes_written": n,
+                      "launches": steps}), flush=True)
+
+
+def cpu_baseline(w, raw, x, g, nt: int, budget_s: float = 20.0) -> dict:
+    """The oracle chain (RMSNorm, q8, GEMV) on the host over a row sample of the
+    same matrix, single thread; the sample is sized to stay near budget_s."""
+    import numpy as np
+
+    import oracle
+    import q6ksynth
+
+    xn = oracle.rmsnorm(x, g, q6ksynth.RMS_EPS)
+    qs, d = oracle.quant_q8(xn)
+    probe = 2048
+    t0 = time.perf_counter()
+    oracle.mmvq(oracle.RAW, raw[:probe], probe, w.K, qs, d, nthreads=1)
+    per_row = (time.perf_counter() - t0) / probe
+    rows = int(min(w.N, max(probe, budget_s / 3 / per_row)))
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.mmvq(oracle.RAW, raw[:rows], rows, w.K, qs, d, nthreads=1)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    content = rows * w.nbe * 210
+    return {"value": round(content / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {rows} of {w.N} rows of the {w.N}x{w.K} matrix, nt={nt}, "
+                      f"scalar C oracle GEMV (fp64), single thread, median of 3 runs "
+                      f"({t:.2f} s each); RMSNorm and q8 on the host excluded",
+            "us_per_gemv_equiv": round(t / rows * w.N * 1e6, 1)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--nt", type=int, default=1, help="activation rows per step (1 or 4)")
+    ap.add_argument("--workload", default="lm_head")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (the path is measured on one GPU's share at its "
+              f"real shape); --gpus {args.gpus} is not supported", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import q6ksynth
+    import quantized_decode_gemv_amd as q
+
+    if args.copy_calib:
+        copy_calib(args.steps)
+        return 0
+
+    dev = "cuda:0"
+    w = q6ksynth.WORKLOADS[args.workload]
+    N, K, nt = w.N, w.K, args.nt
+    log(f"bench: {w.name} N={N} K={K} nt={nt} steps={args.steps} warmup={args.warmup}")
+
+    raw = q6ksynth.weights(w)
+    dpl_bytes = q.q6k_dpl_bytes(N, K)
+    copies = max(2, math.ceil(ROTATE_BYTES / dpl_bytes)) if dpl_bytes < ROTATE_BYTES else 2
+    copies = min(copies, 4096)
+    raw_d = torch.from_numpy(raw.reshape(-1)).to(dev)
+    W0 = torch.empty(dpl_bytes, dtype=torch.uint8, device=dev)
+    q.repack_q6k_dpl(raw_d, W0, N, K)
+    del raw_d
+    Ws = [W0] + [W0.clone() for _ in range(copies - 1)]
+
+    x = q6ksynth.activations(w, nt)
+    g = q6ksynth.gamma(K, q6ksynth.gamma_seed(w))
+    x_d = torch.from_numpy(x).to(dev)
+    g_d = torch.from_numpy(g).to(dev)
+    y_norm = torch.empty((nt, K), dtype=torch.float32, device=dev)
+    plane = torch.empty(q.q8_plane_bytes(K, nt), dtype=torch.uint8, device=dev)
+    y = torch.empty((nt, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        if w.producer == "rmsnorm":
+            q.rmsnorm_quant_q8(x_d, g_d, q6ksynth.RMS_EPS, y_norm, plane, K, nt, stream)
+        else:
+            q.quant_q8(x_d, plane, K, nt, stream)
+        if ev is not None:
+            ev[0].record(stream)
+        q.mmvq_q6k_q8(Ws[i % copies], plane, y, N, K, nt, stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    kern_us = statistics.mean(kern_ms) * 1e3
+    kern_med_us = statistics.median(kern_ms) * 1e3
+
+    content = w.content_bytes
+    value = content / (ms_per_step * 1e-3) / 1e9
+    achieved = content / (kern_us * 1e-6) / 1e9
+    traffic = recorded_traffic(nt)
+    plan = q.mmvq_plan(N, K, nt, torch.cuda.get_device_properties(0).multi_processor_count)
+
+    out = {
+        "metric": "q6_K MMVQ content GB/s and % of HBM peak; us per GEMV at lm_head shape",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / PAGES_LM_HEAD_GBS, 3) if (w.name == "lm_head" and nt == 1) else None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} q6_K GEMV N={N} K={K} nt={nt}: "
+                               f"{'fused RMSNorm->q8' if w.producer == 'rmsnorm' else 'q8'} "
+                               f"producer + dpl q6_K x q8 MMVQ",
+                   "N": N, "K": K, "nt": nt, "content_bytes": content,
+                   "dpl_bytes": dpl_bytes, "weight_copies": copies},
+        "us_per_gemv": round(kern_us, 2),
+        "us_per_gemv_median": round(kern_med_us, 2),
+        "pct_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "mmvq_plan": plan,
+        "kernel_sha": kernel_hash(),
+        "baseline_note": "vs_baseline divides by the pages' 250.0 GB/s dpl lm_head content "
+                         "rate, measured on an NVIDIA GB10: context, not a target",
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the oracle on the host")
+        out["cpu_baseline"] = cpu_baseline(w, raw, x, g, nt)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,146 @@
+/*
+ * q6kdpl.h -- C ABI of libq6kdpl.so: the q6_K x q8 batch-1 decode GEMV (MMVQ) over
+ * the dense split-plane ("dpl") row layout, and its q8 activation producers, for
+ * AMD MI355X (gfx950).
+ *
+ * Sources (page titles; sections cited at each entry point):
+ *   [D4-4] "76 · D4-4 -- the endgame kernel session: dpl dense split-plane q6_K
+ *           decode MMVQ lands (bitwise)"
+ *   [D4-2] "74 · D4-2 -- B0 latent correctness fix + all bitwise occupancy/prefetch
+ *           axes closed"
+ *   [D3-5] "70 · D3-5 -- decode-alignment plan Stage 1: fused-producer decode
+ *           A-quantize"
+ *
+ * Conventions for every entry point:
+ *  - Return 0 (Q6K_OK) on success, a negative Q6K_E_* code on failure. Every
+ *    argument is validated before any device work is queued; on an error nothing
+ *    is launched and no output byte is written. Text: q6k_strerror(code).
+ *  - Device entry points take device pointers (hipMalloc'd memory, e.g. a torch
+ *    tensor's data_ptr()) and `stream`, a hipStream_t passed as void* (NULL means
+ *    the null stream of the current device). They only queue work on `stream`
+ *    and return without synchronising; results are visible after the stream is
+ *    synchronised. Host entry points take host pointers and run synchronously.
+ *  - The caller owns every buffer. The library allocates no memory, keeps no
+ *    cache and reads no environment; calls are reentrant. Calls that share an
+ *    output buffer must be ordered by the caller.
+ *  - Sizes: K is the row length (number of weights per row), N the number of
+ *    rows, nt the number of activation rows ("tokens"). Shape limits:
+ *    1 <= N <= Q6K_MAX_N, 1 <= nt <= Q6K_MAX_NT, 0 < K <= Q6K_MAX_K, and K a
+ *    multiple of 256 for weights (K a multiple of 32 for the producers).
+ *    Anything else is Q6K_E_SHAPE -- there is no silent fallback and no clipping.
+ *
+ * Data layouts (all little-endian):
+ *  raw q6_K row: K/256 super-blocks of 210 B: ql[128] (low 4 bits), qh[64] (high
+ *    2 bits), sc[16] (int8 scale per 16 weights), d (fp16 scale) at bytes 208..209
+ *    ([D4-4] §3.2 Excerpt A). Code q = low4 | high2 << 4 in 0..63, weight value
+ *    d * sc * (q - 32).
+ *  dpl row: [ql: nbe*128][qh: nbe*64][sc: nbe*16][d: nbe*2][zero pad], nbe = K/256,
+ *    row stride (nbe*210 + 15) & ~15 bytes; rows back to back ([D4-4] §2 "The dpl
+ *    split-plane's layout ledger", §3.2 Excerpts A and B).
+ *  q8 plane for nt rows of K activations: [qs: int8 nt*K][d8: fp16 nt*(K/32)],
+ *    t-major in both sections: qs[t*K + k], d8[t*(K/32) + k/32]. Block b of 32
+ *    activations of row t is represented by qs * f16(d8) ([D3-5] §3.2). Both
+ *    sections start 16-B aligned when the plane does. Size q8_plane_bytes(K, nt).
+ *  y: float32 [nt][N], y[t*N + r] (the reduction writes output[t*od + row],
+ *    [D4-2] §3.2 Excerpt B).
+ */
+#ifndef Q6KDPL_H
+#define Q6KDPL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q6K_OK 0
+#define Q6K_E_SHAPE (-1) /* N, K or nt out of range, or K not a multiple of 256/32     */
+#define Q6K_E_NULL (-2)  /* a required pointer is NULL                                  */
+#define Q6K_E_ALIGN (-3) /* a pointer is not 16-byte aligned                            */
+#define Q6K_E_ALIAS (-4) /* an output byte range overlaps an input byte range           */
+#define Q6K_E_HIP (-5)   /* the HIP runtime refused a launch or a device query          */
+
+#define Q6K_MAX_N ((int64_t)1 << 30)
+#define Q6K_MAX_K ((int64_t)1 << 20)
+#define Q6K_MAX_NT 256
+
+/* Text for a return code (static storage; never NULL). */
+const char *q6k_strerror(int code);
+
+/* Library version, e.g. "q6kdpl 0.1 gfx950". */
+const char *q6k_version(void);
+
+/* dpl row stride in bytes, ((K/256)*210 + 15) & ~15 ([D4-4] §2: nbe 54 -> 11344).
+ * Returns 0 when K is not a positive multiple of 256 (or above Q6K_MAX_K). */
+size_t q6k_dpl_row_stride(int64_t K);
+
+/* Bytes of a dpl matrix: N * q6k_dpl_row_stride(K); 0 on a bad shape. */
+size_t q6k_dpl_bytes(int64_t N, int64_t K);
+
+/* Bytes of a raw q6_K matrix: N * (K/256) * 210; 0 on a bad shape. */
+size_t q6k_raw_bytes(int64_t N, int64_t K);
+
+/* Bytes of a q8 plane: nt*K + nt*(K/32)*2; 0 when K is not a positive multiple of
+ * 32 or nt is out of range. */
+size_t q8_plane_bytes(int64_t K, int nt);
+
+/* Host repack raw -> dpl ([D4-4] §3.2 Excerpt A: per row and block, ql, qh, sc, d
+ * are copied into their planes; the row tail after nbe*210 bytes is zeroed).
+ * raw: q6k_raw_bytes(N, K) host bytes; dpl: q6k_dpl_bytes(N, K) host bytes, every
+ * byte written. The ranges must not overlap (Q6K_E_ALIAS). No alignment needed. */
+int repack_q6k_dpl_host(const uint8_t *raw, uint8_t *dpl, int64_t N, int64_t K);
+
+/* Host inverse of repack_q6k_dpl_host (dpl -> raw; pad bytes are ignored). */
+int unpack_q6k_dpl_host(const uint8_t *dpl, uint8_t *raw, int64_t N, int64_t K);
+
+/* Device repack raw -> dpl, byte-identical to repack_q6k_dpl_host. raw_dev needs
+ * no alignment; dpl_dev must be 16-byte aligned. Every byte of dpl_dev
+ * (q6k_dpl_bytes(N, K)) is written, pad bytes with zero. */
+int repack_q6k_dpl(const void *raw_dev, void *dpl_dev, int64_t N, int64_t K, void *stream);
+
+/* Standalone q8 producer ([D3-5] §3.2, the per-32-block body): for each block of
+ * 32 floats, amax = max|x|, d = amax/127 (f32), di = d != 0 ? 1/d : 0 (f32),
+ * q = clamp(rint(x*di), -128, 127) with ties to even; stores qs and f16(d).
+ * x: float32 [nt][K] device, 16-B aligned, finite values. q8: q8_plane_bytes(K, nt)
+ * device bytes, 16-B aligned. K must be a multiple of 32. */
+int quant_q8(const float *x, void *q8, int64_t K, int nt, void *stream);
+
+/* Fused producer: RMSNorm then q8 ([D3-5] §3.2, the fused rms epilogue):
+ * r = 1/sqrt(mean(x^2) + eps) with the mean summed in fp64 and r rounded once to
+ * f32, y = (x*r)*gamma in f32, then the q8 body of quant_q8 applied to y.
+ * x: float32 [nt][K]; gamma: float32 [K]; y: float32 [nt][K] (written); q8: as for
+ * quant_q8. All device, 16-B aligned; y and q8 may not overlap x, gamma or each
+ * other. The q8 bytes equal quant_q8 applied to the y this call writes. */
+int rmsnorm_quant_q8(const float *x, const float *gamma, float eps, float *y, void *q8,
+                     int64_t K, int nt, void *stream);
+
+/* The MMVQ: y[t][r] = sum over super-blocks b and sub-blocks j of
+ * f16(d_rb) * sc_rbj * f16(d8_t,8b+j/2) * D_trbj, with D the exact int32 dot of the
+ * 16 codes (q - 32) and the 16 int8 activations of sub-block j ([D4-2] §3.2
+ * Excerpt C, the per-unit accumulation; [D4-4] §3.2 Excerpt B, the dpl unit load).
+ * Sub-block dots are exact; scaling and summation are f32 (error well inside
+ * 1e-5 * sum|terms|). Every unit of every row is covered for every N, K, nt in
+ * range (no shape reaches a kernel that skips work; [D4-2] §2).
+ * w_dpl: q6k_dpl_bytes(N, K) device bytes, 16-B aligned; q8: q8_plane_bytes(K, nt)
+ * device bytes, 16-B aligned; y: float32 [nt][N] device, 16-B aligned, written. */
+int mmvq_q6k_q8(const void *w_dpl, const void *q8, float *y, int64_t N, int64_t K, int nt,
+                void *stream);
+
+/* Test entry: the exact sub-block dots D of mmvq_q6k_q8, dots[(t*N + r)*(K/16) + j]
+ * (int32, device, 16-B aligned, nt*N*(K/16) entries). Same inputs as mmvq_q6k_q8. */
+int mmvq_q6k_q8_subdots(const void *w_dpl, const void *q8, int32_t *dots, int64_t N, int64_t K,
+                        int nt, void *stream);
+
+/* Diagnostics: how mmvq_q6k_q8 runs a shape on a device with num_cu compute units.
+ * out5[0] = workgroups per launch (256 threads each), out5[1] = low-bit chunks per
+ * lane per row, out5[2] = 1 for a fixed-length kernel (0: the generic stepping
+ * kernel), out5[3] = 1 when activation operands stay in registers across rows,
+ * out5[4] = launches (one per group of up to 4 token columns). Host only. */
+int q6k_mmvq_plan(int64_t N, int64_t K, int nt, int num_cu, int32_t *out5);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q6KDPL_H */

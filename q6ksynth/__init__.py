@@ -64,18 +64,29 @@ def gamma_seed(w: Workload) -> int:
     return 1000 * w.index + 999
 
 
+def _random_bytes(rng: np.random.Generator, n: int) -> np.ndarray:
+    """n uniform random bytes: the generator's raw 64-bit outputs, little-endian."""
+    words = rng.bit_generator.random_raw((n + 7) // 8)
+    return words.astype("<u8", copy=False).view(np.uint8)[:n]
+
+
 def raw_q6k(N: int, K: int, seed: int) -> np.ndarray:
-    """Random raw GGUF q6_K rows, uint8 [N, (K/256)*210]."""
+    """Random raw GGUF q6_K rows, uint8 [N, (K/256)*210].
+
+    Low/high bit bytes are uniform random bytes; each int8 sub-block scale is a
+    uniform byte masked to 6 bits minus 32 (exactly uniform on [-32, 31]); the fp16
+    super-block scale is fp16(|N(0,1)| * 1e-3)."""
     assert K > 0 and K % 256 == 0 and N >= 0
     nbe = K // 256
     rng = np.random.default_rng(seed)
-    out = np.empty((N, nbe, BLOCK_BYTES), np.uint8)
-    out[:, :, :QL_BYTES + QH_BYTES] = rng.integers(
-        0, 256, size=(N, nbe, QL_BYTES + QH_BYTES), dtype=np.uint8)
-    sc = rng.integers(-32, 32, size=(N, nbe, SC_BYTES), dtype=np.int8)
-    out[:, :, 192:208] = sc.view(np.uint8)
-    d = (np.abs(rng.standard_normal((N, nbe))) * 1e-3).astype(np.float16)
-    out[:, :, 208:210] = d.view(np.uint8).reshape(N, nbe, 2)
+    nblk = N * nbe
+    out = np.empty((nblk, BLOCK_BYTES), np.uint8)
+    out[:, :QL_BYTES + QH_BYTES] = _random_bytes(rng, nblk * (QL_BYTES + QH_BYTES)).reshape(
+        nblk, QL_BYTES + QH_BYTES)
+    sc = (_random_bytes(rng, nblk * SC_BYTES) & 63).astype(np.int16) - 32
+    out[:, 192:208] = sc.astype(np.int8).view(np.uint8).reshape(nblk, SC_BYTES)
+    d = (np.abs(rng.standard_normal(nblk)) * 1e-3).astype(np.float16)
+    out[:, 208:210] = d.view(np.uint8).reshape(nblk, 2)
     return out.reshape(N, nbe * BLOCK_BYTES)
 
 

@@ -1,0 +1,186 @@
+"""ctypes marshalling for libq6kdpl.so (see include/q6kdpl.h for the contract)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import numpy as np
+import torch  # loads the HIP runtime this library then shares (same soname)
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libq6kdpl.so")
+
+Q6K_MAX_N = 1 << 30
+Q6K_MAX_K = 1 << 20
+Q6K_MAX_NT = 256
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_INT = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+_SIGS = {
+    "q6k_strerror": (ctypes.c_char_p, [_INT]),
+    "q6k_version": (ctypes.c_char_p, []),
+    "q6k_dpl_row_stride": (_SZ, [_I64]),
+    "q6k_dpl_bytes": (_SZ, [_I64, _I64]),
+    "q6k_raw_bytes": (_SZ, [_I64, _I64]),
+    "q8_plane_bytes": (_SZ, [_I64, _INT]),
+    "repack_q6k_dpl_host": (_INT, [_P, _P, _I64, _I64]),
+    "unpack_q6k_dpl_host": (_INT, [_P, _P, _I64, _I64]),
+    "repack_q6k_dpl": (_INT, [_P, _P, _I64, _I64, _P]),
+    "quant_q8": (_INT, [_P, _P, _I64, _INT, _P]),
+    "rmsnorm_quant_q8": (_INT, [_P, _P, ctypes.c_float, _P, _P, _I64, _INT, _P]),
+    "mmvq_q6k_q8": (_INT, [_P, _P, _P, _I64, _I64, _INT, _P]),
+    "mmvq_q6k_q8_subdots": (_INT, [_P, _P, _P, _I64, _I64, _INT, _P]),
+    "q6k_mmvq_plan": (_INT, [_I64, _I64, _INT, _INT, _P]),
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class Q6kError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        msg = lib().q6k_strerror(code).decode()
+        super().__init__(f"{fn}: error {code}: {msg}")
+
+
+def load(build_if_missing: bool = True) -> ctypes.CDLL:
+    """Load the in-tree library; build it first only if it does not exist."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            if not build_if_missing:
+                raise FileNotFoundError(f"{LIB_PATH} is not built")
+            from . import build as _build
+            _build.build()
+        dll = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(dll, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = dll
+        return dll
+
+
+def lib() -> ctypes.CDLL:
+    return _lib if _lib is not None else load()
+
+
+def _addr(p) -> int | None:
+    """Device/host address of a tensor, numpy array or integer (None for NULL)."""
+    if p is None:
+        return None
+    if isinstance(p, torch.Tensor):
+        return p.data_ptr()
+    if isinstance(p, np.ndarray):
+        return p.ctypes.data
+    return int(p)
+
+
+def _need(name: str, t, nbytes: int, device: bool = True) -> None:
+    """Refuse a torch tensor that is smaller than the bytes the call touches, not
+    contiguous, or on the wrong side of the bus. Integers pass through unchecked."""
+    if not isinstance(t, torch.Tensor):
+        return
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name}: buffer holds {have} bytes, the call touches {nbytes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: buffer must be contiguous")
+    if device != t.is_cuda:
+        raise ValueError(f"{name}: buffer must be on the {'GPU' if device else 'host'}")
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _call(name: str, *args) -> None:
+    rc = getattr(lib(), name)(*args)
+    if rc != 0:
+        raise Q6kError(name, rc)
+
+
+def q6k_version() -> str:
+    return lib().q6k_version().decode()
+
+
+def q6k_dpl_row_stride(K: int) -> int:
+    return int(lib().q6k_dpl_row_stride(K))
+
+
+def q6k_dpl_bytes(N: int, K: int) -> int:
+    return int(lib().q6k_dpl_bytes(N, K))
+
+
+def q6k_raw_bytes(N: int, K: int) -> int:
+    return int(lib().q6k_raw_bytes(N, K))
+
+
+def q8_plane_bytes(K: int, nt: int) -> int:
+    return int(lib().q8_plane_bytes(K, nt))
+
+
+def repack_q6k_dpl_host(raw, dpl, N: int, K: int) -> None:
+    _need("raw", raw, q6k_raw_bytes(N, K), device=False)
+    _need("dpl", dpl, q6k_dpl_bytes(N, K), device=False)
+    _call("repack_q6k_dpl_host", _addr(raw), _addr(dpl), N, K)
+
+
+def unpack_q6k_dpl_host(dpl, raw, N: int, K: int) -> None:
+    _need("dpl", dpl, q6k_dpl_bytes(N, K), device=False)
+    _need("raw", raw, q6k_raw_bytes(N, K), device=False)
+    _call("unpack_q6k_dpl_host", _addr(dpl), _addr(raw), N, K)
+
+
+def repack_q6k_dpl(raw_dev, dpl_dev, N: int, K: int, stream=None) -> None:
+    _need("raw_dev", raw_dev, q6k_raw_bytes(N, K))
+    _need("dpl_dev", dpl_dev, q6k_dpl_bytes(N, K))
+    _call("repack_q6k_dpl", _addr(raw_dev), _addr(dpl_dev), N, K, _stream(stream))
+
+
+def quant_q8(x, q8, K: int, nt: int, stream=None) -> None:
+    _need("x", x, 4 * K * max(nt, 0))
+    _need("q8", q8, q8_plane_bytes(K, nt))
+    _call("quant_q8", _addr(x), _addr(q8), K, nt, _stream(stream))
+
+
+def rmsnorm_quant_q8(x, gamma, eps: float, y, q8, K: int, nt: int, stream=None) -> None:
+    _need("x", x, 4 * K * max(nt, 0))
+    _need("gamma", gamma, 4 * K)
+    _need("y", y, 4 * K * max(nt, 0))
+    _need("q8", q8, q8_plane_bytes(K, nt))
+    _call("rmsnorm_quant_q8", _addr(x), _addr(gamma), float(eps), _addr(y), _addr(q8), K, nt,
+          _stream(stream))
+
+
+def mmvq_q6k_q8(w_dpl, q8, y, N: int, K: int, nt: int, stream=None) -> None:
+    _need("w_dpl", w_dpl, q6k_dpl_bytes(N, K))
+    _need("q8", q8, q8_plane_bytes(K, nt))
+    _need("y", y, 4 * max(N, 0) * max(nt, 0))
+    _call("mmvq_q6k_q8", _addr(w_dpl), _addr(q8), _addr(y), N, K, nt, _stream(stream))
+
+
+def mmvq_q6k_q8_subdots(w_dpl, q8, dots, N: int, K: int, nt: int, stream=None) -> None:
+    _need("w_dpl", w_dpl, q6k_dpl_bytes(N, K))
+    _need("q8", q8, q8_plane_bytes(K, nt))
+    _need("dots", dots, 4 * max(N, 0) * max(nt, 0) * max(K // 16, 0))
+    _call("mmvq_q6k_q8_subdots", _addr(w_dpl), _addr(q8), _addr(dots), N, K, nt,
+          _stream(stream))
+
+
+def mmvq_plan(N: int, K: int, nt: int, num_cu: int) -> dict:
+    out = (ctypes.c_int32 * 5)()
+    _call("q6k_mmvq_plan", N, K, nt, num_cu, ctypes.addressof(out))
+    return dict(grid=out[0], cpl=out[1], unrolled=bool(out[2]), hoist=bool(out[3]),
+                launches=out[4])

@@ -1,0 +1,232 @@
+// abi.hip -- the extern "C" entry points of libq6kdpl.so (include/q6kdpl.h).
+//
+// Each entry point validates every argument (shape, NULL, 16-byte alignment,
+// output/input overlap) before queuing anything, then queues its kernels on the
+// caller's stream and returns. No entry point allocates, synchronises or caches
+// data; the only process-wide state is a per-device table of compute-unit counts.
+
+#include <atomic>
+
+#include "../../include/q6kdpl.h"
+#include "q6k_internal.h"
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb)
+{
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return na && nb && a0 < b0 + nb && b0 < a0 + na;
+}
+
+bool weight_shape_ok(int64_t N, int64_t K)
+{
+    return N >= 1 && N <= Q6K_MAX_N && K > 0 && K <= Q6K_MAX_K && K % 256 == 0;
+}
+
+bool act_shape_ok(int64_t K, int nt)
+{
+    return K > 0 && K <= Q6K_MAX_K && K % 32 == 0 && nt >= 1 && nt <= Q6K_MAX_NT;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? Q6K_OK : Q6K_E_HIP; }
+
+constexpr int MAX_DEV = 64;
+std::atomic<int> g_cu_count[MAX_DEV];
+
+// Compute units of the device that owns `s` (the current device for NULL).
+int cu_count(hipStream_t s, int *cu)
+{
+    int dev = 0;
+    if (s != nullptr) {
+        if (hipStreamGetDevice(s, &dev) != hipSuccess)
+            return Q6K_E_HIP;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return Q6K_E_HIP;
+    }
+    if (dev < 0 || dev >= MAX_DEV)
+        return Q6K_E_HIP;
+    int n = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            return Q6K_E_HIP;
+        g_cu_count[dev].store(n, std::memory_order_relaxed);
+    }
+    *cu = n;
+    return Q6K_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *q6k_strerror(int code)
+{
+    switch (code) {
+    case Q6K_OK: return "ok";
+    case Q6K_E_SHAPE: return "shape out of range (N, K or nt; K must be a multiple of 256 for "
+                             "weights, of 32 for activations)";
+    case Q6K_E_NULL: return "a required pointer is NULL";
+    case Q6K_E_ALIGN: return "a device pointer is not 16-byte aligned";
+    case Q6K_E_ALIAS: return "an output range overlaps an input range";
+    case Q6K_E_HIP: return "the HIP runtime refused a launch or device query";
+    default: return "unknown q6kdpl error code";
+    }
+}
+
+const char *q6k_version(void) { return "q6kdpl 0.1 gfx950"; }
+
+size_t q6k_dpl_row_stride(int64_t K)
+{
+    if (K <= 0 || K > Q6K_MAX_K || K % 256)
+        return 0;
+    return (size_t)(((K / 256) * 210 + 15) & ~(int64_t)15);
+}
+
+size_t q6k_dpl_bytes(int64_t N, int64_t K)
+{
+    if (!weight_shape_ok(N, K))
+        return 0;
+    return (size_t)N * q6k_dpl_row_stride(K);
+}
+
+size_t q6k_raw_bytes(int64_t N, int64_t K)
+{
+    if (!weight_shape_ok(N, K))
+        return 0;
+    return (size_t)N * (size_t)(K / 256) * 210u;
+}
+
+size_t q8_plane_bytes(int64_t K, int nt)
+{
+    if (!act_shape_ok(K, nt))
+        return 0;
+    return (size_t)nt * (size_t)K + (size_t)nt * (size_t)(K / 32) * 2u;
+}
+
+int repack_q6k_dpl_host(const uint8_t *raw, uint8_t *dpl, int64_t N, int64_t K)
+{
+    if (!weight_shape_ok(N, K))
+        return Q6K_E_SHAPE;
+    if (!raw || !dpl)
+        return Q6K_E_NULL;
+    if (overlap(raw, q6k_raw_bytes(N, K), dpl, q6k_dpl_bytes(N, K)))
+        return Q6K_E_ALIAS;
+    q6k::repack_host(raw, dpl, N, K);
+    return Q6K_OK;
+}
+
+int unpack_q6k_dpl_host(const uint8_t *dpl, uint8_t *raw, int64_t N, int64_t K)
+{
+    if (!weight_shape_ok(N, K))
+        return Q6K_E_SHAPE;
+    if (!raw || !dpl)
+        return Q6K_E_NULL;
+    if (overlap(raw, q6k_raw_bytes(N, K), dpl, q6k_dpl_bytes(N, K)))
+        return Q6K_E_ALIAS;
+    q6k::unpack_host(dpl, raw, N, K);
+    return Q6K_OK;
+}
+
+int repack_q6k_dpl(const void *raw_dev, void *dpl_dev, int64_t N, int64_t K, void *stream)
+{
+    if (!weight_shape_ok(N, K))
+        return Q6K_E_SHAPE;
+    if (!raw_dev || !dpl_dev)
+        return Q6K_E_NULL;
+    if (!aligned16(dpl_dev))
+        return Q6K_E_ALIGN;
+    if (overlap(raw_dev, q6k_raw_bytes(N, K), dpl_dev, q6k_dpl_bytes(N, K)))
+        return Q6K_E_ALIAS;
+    return from_hip(q6k::launch_repack((const uint8_t *)raw_dev, (uint8_t *)dpl_dev, N, K,
+                                       (hipStream_t)stream));
+}
+
+int quant_q8(const float *x, void *q8, int64_t K, int nt, void *stream)
+{
+    if (!act_shape_ok(K, nt))
+        return Q6K_E_SHAPE;
+    if (!x || !q8)
+        return Q6K_E_NULL;
+    if (!aligned16(x) || !aligned16(q8))
+        return Q6K_E_ALIGN;
+    if (overlap(x, (size_t)nt * K * 4u, q8, q8_plane_bytes(K, nt)))
+        return Q6K_E_ALIAS;
+    return from_hip(q6k::launch_quant(x, (uint8_t *)q8, K, nt, (hipStream_t)stream));
+}
+
+int rmsnorm_quant_q8(const float *x, const float *gamma, float eps, float *y, void *q8,
+                     int64_t K, int nt, void *stream)
+{
+    if (!act_shape_ok(K, nt))
+        return Q6K_E_SHAPE;
+    if (!x || !gamma || !y || !q8)
+        return Q6K_E_NULL;
+    if (!aligned16(x) || !aligned16(gamma) || !aligned16(y) || !aligned16(q8))
+        return Q6K_E_ALIGN;
+    const size_t nx = (size_t)nt * K * 4u, ng = (size_t)K * 4u, nq = q8_plane_bytes(K, nt);
+    if (overlap(y, nx, x, nx) || overlap(y, nx, gamma, ng) || overlap(q8, nq, x, nx) ||
+        overlap(q8, nq, gamma, ng) || overlap(q8, nq, y, nx))
+        return Q6K_E_ALIAS;
+    return from_hip(
+        q6k::launch_rmsnorm_quant(x, gamma, eps, y, (uint8_t *)q8, K, nt, (hipStream_t)stream));
+}
+
+int mmvq_q6k_q8(const void *w_dpl, const void *q8, float *y, int64_t N, int64_t K, int nt,
+                void *stream)
+{
+    if (!weight_shape_ok(N, K) || !act_shape_ok(K, nt))
+        return Q6K_E_SHAPE;
+    if (!w_dpl || !q8 || !y)
+        return Q6K_E_NULL;
+    if (!aligned16(w_dpl) || !aligned16(q8) || !aligned16(y))
+        return Q6K_E_ALIGN;
+    const size_t ny = (size_t)nt * N * 4u;
+    if (overlap(y, ny, w_dpl, q6k_dpl_bytes(N, K)) || overlap(y, ny, q8, q8_plane_bytes(K, nt)))
+        return Q6K_E_ALIAS;
+    int cu = 0;
+    int rc = cu_count((hipStream_t)stream, &cu);
+    if (rc != Q6K_OK)
+        return rc;
+    return from_hip(q6k::launch_mmvq((const uint8_t *)w_dpl, (const uint8_t *)q8, y, N, K, nt,
+                                     cu, (hipStream_t)stream));
+}
+
+int mmvq_q6k_q8_subdots(const void *w_dpl, const void *q8, int32_t *dots, int64_t N, int64_t K,
+                        int nt, void *stream)
+{
+    if (!weight_shape_ok(N, K) || !act_shape_ok(K, nt))
+        return Q6K_E_SHAPE;
+    if (!w_dpl || !q8 || !dots)
+        return Q6K_E_NULL;
+    if (!aligned16(w_dpl) || !aligned16(q8) || !aligned16(dots))
+        return Q6K_E_ALIGN;
+    const size_t nd = (size_t)nt * N * (K / 16) * 4u;
+    if (overlap(dots, nd, w_dpl, q6k_dpl_bytes(N, K)) || overlap(dots, nd, q8, q8_plane_bytes(K, nt)))
+        return Q6K_E_ALIAS;
+    int cu = 0;
+    int rc = cu_count((hipStream_t)stream, &cu);
+    if (rc != Q6K_OK)
+        return rc;
+    return from_hip(q6k::launch_subdots((const uint8_t *)w_dpl, (const uint8_t *)q8, dots, N, K,
+                                        nt, cu, (hipStream_t)stream));
+}
+
+int q6k_mmvq_plan(int64_t N, int64_t K, int nt, int num_cu, int32_t *out5)
+{
+    if (!weight_shape_ok(N, K) || !act_shape_ok(K, nt) || num_cu < 1)
+        return Q6K_E_SHAPE;
+    if (!out5)
+        return Q6K_E_NULL;
+    const q6k::MmvqPlan p = q6k::plan_mmvq(N, K, nt, num_cu);
+    out5[0] = (int32_t)p.grid;
+    out5[1] = p.cpl;
+    out5[2] = p.unrolled;
+    out5[3] = p.hoist;
+    out5[4] = p.launches;
+    return Q6K_OK;
+}
+
+}  // extern "C"

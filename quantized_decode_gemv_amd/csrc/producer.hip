@@ -1,0 +1,165 @@
+// producer.hip -- q8 activation producers for gfx950: the standalone quantizer and
+// the fused RMSNorm -> q8 producer.
+//
+// The q8 body follows the per-32-block quantizer of D3-5 §3.2: amax = max|x|,
+// d = amax/127 (f32 division), di = d != 0 ? 1/d : 0 (f32 division),
+// q = clamp(rint(x*di), -128, 127) with ties to even, stored scale f16(d).
+// HIP's default f32 division and rintf (v_rndne_f32) are IEEE, and there is no
+// add next to a product to contract, so every byte follows from its own input value
+// and its block's amax (max is exact under any association).
+//
+// Thread geometry: a lane holds 4 consecutive values (one float4), 8 consecutive
+// lanes hold one 32-value block, and the block's amax is an xor-butterfly max over
+// those 8 lanes. Every lane of a wave runs the butterfly; lanes past the end carry
+// zeros and store nothing, so no lane leaves before a cross-lane step.
+
+#include "q6k_internal.h"
+
+namespace q6k {
+
+namespace {
+
+struct Q8Out {
+    uint32_t packed;   // 4 int8 codes
+    uint16_t d16;      // f16 block scale (meaningful on every lane of the group)
+};
+
+__device__ __forceinline__ int q_of(float v, float di)
+{
+    int q = (int)rintf(v * di);
+    return q < -128 ? -128 : (q > 127 ? 127 : q);
+}
+
+// All 64 lanes must call this together; lanes 8m..8m+7 form one block.
+__device__ __forceinline__ Q8Out quant_group8(float4 v)
+{
+    float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    m = fmaxf(m, __shfl_xor(m, 4));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    m = fmaxf(m, __shfl_xor(m, 1));
+    const float d = m / 127.0f;
+    const float di = (d != 0.0f) ? 1.0f / d : 0.0f;
+    Q8Out o;
+    o.packed = (uint32_t)(uint8_t)q_of(v.x, di) | ((uint32_t)(uint8_t)q_of(v.y, di) << 8) |
+               ((uint32_t)(uint8_t)q_of(v.z, di) << 16) | ((uint32_t)(uint8_t)q_of(v.w, di) << 24);
+    o.d16 = __builtin_bit_cast(uint16_t, (_Float16)d);
+    return o;
+}
+
+constexpr int QWG = 256;
+
+// x: nt*K floats (t-major), one float4 per lane over the flattened array; the q8
+// plane's two sections are t-major too, so flat index f maps to qs[4f..4f+3] and
+// block f/8.
+__global__ __launch_bounds__(QWG) void quant_q8_kernel(const float4 *__restrict__ x,
+                                                       uint32_t *__restrict__ qs,
+                                                       uint16_t *__restrict__ d8, uint32_t nf4)
+{
+    const uint32_t f = blockIdx.x * QWG + threadIdx.x;
+    const bool live = f < nf4;
+    const float4 v = live ? x[f] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const Q8Out o = quant_group8(v);
+    if (live) {
+        qs[f] = o.packed;
+        if ((f & 7u) == 0)
+            d8[f >> 3] = o.d16;
+    }
+}
+
+// One workgroup per token row. Pass 1: fp64 sum of squares (each x^2 is exact in
+// fp64), reduced in a fixed order; r = f32(1 / sqrt(mean + eps)). Pass 2: y = (x*r)*g
+// in f32, stored, and quantized from registers by the q8 body (the same values the
+// row holds in memory, so the bytes equal quant_q8 applied to y).
+template <int BS>
+__global__ __launch_bounds__(BS) void rmsnorm_quant_kernel(const float4 *__restrict__ x,
+                                                           const float4 *__restrict__ g,
+                                                           float eps, float4 *__restrict__ y,
+                                                           uint32_t *__restrict__ qs,
+                                                           uint16_t *__restrict__ d8, uint32_t K)
+{
+    const uint32_t t = blockIdx.x;
+    const uint32_t K4 = K / 4u;
+    const float4 *xr = x + (size_t)t * K4;
+    double ss = 0.0;
+    for (uint32_t f = threadIdx.x; f < K4; f += BS) {
+        const float4 v = xr[f];
+        ss += (double)v.x * (double)v.x;
+        ss += (double)v.y * (double)v.y;
+        ss += (double)v.z * (double)v.z;
+        ss += (double)v.w * (double)v.w;
+    }
+    ss += __shfl_xor(ss, 32);
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 8);
+    ss += __shfl_xor(ss, 4);
+    ss += __shfl_xor(ss, 2);
+    ss += __shfl_xor(ss, 1);
+    __shared__ double part[BS / 64];
+    if ((threadIdx.x & 63u) == 0)
+        part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    double tot = 0.0;
+#pragma unroll
+    for (int i = 0; i < BS / 64; ++i)
+        tot += part[i];
+    const float r = (float)(1.0 / sqrt(tot / (double)K + (double)eps));
+
+    float4 *yr = y + (size_t)t * K4;
+    uint32_t *qr = qs + (size_t)t * K4;
+    uint16_t *dr = d8 + (size_t)t * (K / 32u);
+    const uint32_t iters = (K4 + BS - 1) / BS;
+    for (uint32_t it = 0; it < iters; ++it) {
+        const uint32_t f = it * BS + threadIdx.x;
+        const bool live = f < K4;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (live) {
+            const float4 xv = xr[f];
+            const float4 gv = g[f];
+            v.x = (xv.x * r) * gv.x;
+            v.y = (xv.y * r) * gv.y;
+            v.z = (xv.z * r) * gv.z;
+            v.w = (xv.w * r) * gv.w;
+            yr[f] = v;
+        }
+        const Q8Out o = quant_group8(v);
+        if (live) {
+            qr[f] = o.packed;
+            if ((f & 7u) == 0)
+                dr[f >> 3] = o.d16;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quant(const float *x, uint8_t *q8, int64_t K, int nt, hipStream_t s)
+{
+    const float4 *x4 = reinterpret_cast<const float4 *>(x);
+    uint32_t *qs = reinterpret_cast<uint32_t *>(q8);
+    uint16_t *d8 = reinterpret_cast<uint16_t *>(q8 + (size_t)nt * K);
+    uint32_t nf4 = (uint32_t)((int64_t)nt * K / 4);
+    const uint32_t grid = (nf4 + QWG - 1) / QWG;
+    void *args[] = {(void *)&x4, (void *)&qs, (void *)&d8, (void *)&nf4};
+    return hipLaunchKernel((const void *)quant_q8_kernel, dim3(grid), dim3(QWG), args, 0, s);
+}
+
+hipError_t launch_rmsnorm_quant(const float *x, const float *gamma, float eps, float *y,
+                                uint8_t *q8, int64_t K, int nt, hipStream_t s)
+{
+    const float4 *x4 = reinterpret_cast<const float4 *>(x);
+    const float4 *g4 = reinterpret_cast<const float4 *>(gamma);
+    float4 *y4 = reinterpret_cast<float4 *>(y);
+    uint32_t *qs = reinterpret_cast<uint32_t *>(q8);
+    uint16_t *d8 = reinterpret_cast<uint16_t *>(q8 + (size_t)nt * K);
+    uint32_t Ku = (uint32_t)K;
+    void *args[] = {(void *)&x4, (void *)&g4, (void *)&eps, (void *)&y4,
+                    (void *)&qs, (void *)&d8, (void *)&Ku};
+    // 1024 threads for long rows so each lane holds few float4s; 256 otherwise.
+    if (K >= 8192)
+        return hipLaunchKernel((const void *)rmsnorm_quant_kernel<1024>, dim3(nt), dim3(1024),
+                               args, 0, s);
+    return hipLaunchKernel((const void *)rmsnorm_quant_kernel<256>, dim3(nt), dim3(256), args, 0,
+                           s);
+}
+
+}  // namespace q6k

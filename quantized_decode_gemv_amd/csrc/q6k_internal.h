@@ -1,0 +1,34 @@
+// q6k_internal.h -- launchers shared between the C ABI layer and the kernel files.
+// Shapes and pointers reaching these functions have already been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <utility>
+
+namespace q6k {
+
+// How mmvq_q6k_q8 will run a shape (for tests and reports).
+struct MmvqPlan {
+    uint32_t grid = 0;      // workgroups of 256 threads
+    int cpl = 0;            // low-bit chunks per lane per row
+    bool unrolled = false;  // a fixed-CPL kernel (else the generic stepping kernel)
+    bool hoist = false;     // activation operands held in registers across rows
+    int launches = 0;       // one launch per group of up to 4 token columns
+};
+
+MmvqPlan plan_mmvq(int64_t N, int64_t K, int nt, int num_cu);
+
+hipError_t launch_mmvq(const uint8_t *w, const uint8_t *q8, float *y, int64_t N, int64_t K,
+                       int nt, int num_cu, hipStream_t s);
+hipError_t launch_subdots(const uint8_t *w, const uint8_t *q8, int32_t *dots, int64_t N,
+                          int64_t K, int nt, int num_cu, hipStream_t s);
+hipError_t launch_quant(const float *x, uint8_t *q8, int64_t K, int nt, hipStream_t s);
+hipError_t launch_rmsnorm_quant(const float *x, const float *gamma, float eps, float *y,
+                                uint8_t *q8, int64_t K, int nt, hipStream_t s);
+hipError_t launch_repack(const uint8_t *raw, uint8_t *dpl, int64_t N, int64_t K, hipStream_t s);
+void repack_host(const uint8_t *raw, uint8_t *dpl, int64_t N, int64_t K);
+void unpack_host(const uint8_t *dpl, uint8_t *raw, int64_t N, int64_t K);
+
+}  // namespace q6k

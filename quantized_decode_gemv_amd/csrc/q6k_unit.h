@@ -1,0 +1,152 @@
+// q6k_unit.h -- per-lane work on one 16-byte low-bit chunk of a dpl row (gfx950).
+//
+// A dpl row is [ql: nbe*128][qh: nbe*64][sc: nbe*16][d: nbe*2] (D4-4 §3.2 Excerpt B
+// gives the section bases). The ql plane is cut into 16-byte chunks, chunk Q holding
+// the low bits of 32 codes; a wave64 takes 64 consecutive chunks per instruction,
+// so every low-bit load is one contiguous, 16 B-per-lane, 1 KB request.
+//
+// Chunk Q = 8*kbx + 4*c + 2*s + h (kbx the super-block, c its 128-element half,
+// s = g & 1 of the 32-element unit, h the 16-byte half of the unit's 32-byte
+// window). By the unit-load address formulas of D4-4 §3.2 Excerpt B (low bits of
+// unit (c, g) at kbx*128 + c*64 + (g&1)*32, high bits at kbx*64 + c*32, 2-bit field
+// at shift 2g), the chunk's low nibbles are codes of unit g = s and its high
+// nibbles codes of unit g = s + 2, positions l = 16h .. 16h+15 of both units:
+//   - high bits: the 16 qh bytes at qh plane + 16*(2*(Q>>2) + h); field 2s (low
+//     nibble codes) and 2s + 4 (high nibble codes);
+//   - scales: sub-blocks j = 8c + 2s + h and j + 4 of the block, i.e. bytes (Q & 3)
+//     and (Q & 3) + 4 of the 8-byte scale group at sc plane + 8*(Q>>2);
+//   - activations: the 16 int8 at k = 16*(Q + 4*(Q>>2)) and k + 64, in q8 blocks
+//     4*(Q>>2) + s and that + 2.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q6k {
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t bits)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+// Activation operands of one chunk for one token.
+struct ChunkAct {
+    uint4 xa, xb;   // the 16 int8 activations of each of the chunk's two sub-blocks
+    float da, db;   // their q8 block scales (fp16 values, exact in f32)
+    int na, nb;     // -32 * (sum of the 16 activations): folds the code offset -32 in
+};
+
+// Weight operands of one chunk.
+struct ChunkW {
+    uint4 ql;       // 16 bytes of low bits (32 codes)
+    uint4 qh;       // 16 bytes of high-bit fields
+    uint2 sc;       // the 8-byte scale group
+    uint32_t d;     // fp16 super-block scale bits
+};
+
+__device__ __forceinline__ int sum16_i8(uint4 v)
+{
+    int s = __builtin_amdgcn_sdot4((int)v.x, 0x01010101, 0, false);
+    s = __builtin_amdgcn_sdot4((int)v.y, 0x01010101, s, false);
+    s = __builtin_amdgcn_sdot4((int)v.z, 0x01010101, s, false);
+    return __builtin_amdgcn_sdot4((int)v.w, 0x01010101, s, false);
+}
+
+// qs_t: int8 activations of one token (K entries); d8_t: its fp16 block scales.
+__device__ __forceinline__ ChunkAct load_act(const int8_t *__restrict__ qs_t,
+                                             const uint16_t *__restrict__ d8_t, uint32_t Q)
+{
+    const uint32_t G = Q >> 2;
+    const uint32_t k = 16u * (Q + 4u * G);
+    const uint32_t blk = 4u * G + ((Q >> 1) & 1u);
+    ChunkAct a;
+    a.xa = *reinterpret_cast<const uint4 *>(qs_t + k);
+    a.xb = *reinterpret_cast<const uint4 *>(qs_t + k + 64);
+    a.da = f16_bits_to_f32(d8_t[blk]);
+    a.db = f16_bits_to_f32(d8_t[blk + 2]);
+    a.na = -32 * sum16_i8(a.xa);
+    a.nb = -32 * sum16_i8(a.xb);
+    return a;
+}
+
+// row: start of a dpl row; nbe: super-blocks per row.
+__device__ __forceinline__ ChunkW load_w(const uint8_t *__restrict__ row, uint32_t nbe, uint32_t Q)
+{
+    const uint32_t G = Q >> 2;
+    ChunkW w;
+    w.ql = *reinterpret_cast<const uint4 *>(row + 16u * Q);
+    w.qh = *reinterpret_cast<const uint4 *>(row + 128u * nbe + 16u * (2u * G + (Q & 1u)));
+    w.sc = *reinterpret_cast<const uint2 *>(row + 192u * nbe + 8u * G);
+    w.d = *reinterpret_cast<const uint16_t *>(row + 208u * nbe + 2u * (Q >> 3));
+    return w;
+}
+
+// Four codes per 32-bit word: low nibbles (unit s) or high nibbles (unit s + 2) of
+// the low-bit word, with the matching 2-bit fields of the high-bit word placed at
+// bits 4..5 of each byte. h_sh is the high-bit word shifted right by 2s.
+__device__ __forceinline__ uint32_t codes_lo(uint32_t l, uint32_t h_sh)
+{
+    return (l & 0x0F0F0F0Fu) | ((h_sh << 4) & 0x30303030u);
+}
+__device__ __forceinline__ uint32_t codes_hi(uint32_t l, uint32_t h_sh)
+{
+    return ((l >> 4) & 0x0F0F0F0Fu) | (h_sh & 0x30303030u);
+}
+
+// The chunk's two exact sub-block dots sum (q - 32) * x8: the dot of the unsigned
+// codes with the activations, started from -32 * sum(x8).
+__device__ __forceinline__ void chunk_dots(const ChunkW &w, const ChunkAct &a, uint32_t Q,
+                                           int &Da, int &Db)
+{
+    const uint32_t sh = 2u * ((Q >> 1) & 1u);
+    int da = a.na, db = a.nb;
+    uint32_t h;
+    h = w.qh.x >> sh;
+    da = __builtin_amdgcn_sdot4((int)codes_lo(w.ql.x, h), (int)a.xa.x, da, false);
+    db = __builtin_amdgcn_sdot4((int)codes_hi(w.ql.x, h), (int)a.xb.x, db, false);
+    h = w.qh.y >> sh;
+    da = __builtin_amdgcn_sdot4((int)codes_lo(w.ql.y, h), (int)a.xa.y, da, false);
+    db = __builtin_amdgcn_sdot4((int)codes_hi(w.ql.y, h), (int)a.xb.y, db, false);
+    h = w.qh.z >> sh;
+    da = __builtin_amdgcn_sdot4((int)codes_lo(w.ql.z, h), (int)a.xa.z, da, false);
+    db = __builtin_amdgcn_sdot4((int)codes_hi(w.ql.z, h), (int)a.xb.z, db, false);
+    h = w.qh.w >> sh;
+    da = __builtin_amdgcn_sdot4((int)codes_lo(w.ql.w, h), (int)a.xa.w, da, false);
+    db = __builtin_amdgcn_sdot4((int)codes_hi(w.ql.w, h), (int)a.xb.w, db, false);
+    Da = da;
+    Db = db;
+}
+
+// The chunk's int8 scales of its two sub-blocks.
+__device__ __forceinline__ void chunk_scales(const ChunkW &w, uint32_t Q, int &sa, int &sb)
+{
+    const uint32_t bit = 8u * (Q & 3u);
+    sa = (int)(int8_t)(uint8_t)(w.sc.x >> bit);
+    sb = (int)(int8_t)(uint8_t)(w.sc.y >> bit);
+}
+
+// The chunk's contribution d * (d8a * sa*Da + d8b * sb*Db). sa*Da and sb*Db are
+// exact integers below 2^23, so their f32 conversion is exact.
+__device__ __forceinline__ float chunk_partial(const ChunkW &w, const ChunkAct &a, uint32_t Q)
+{
+    int Da, Db, sa, sb;
+    chunk_dots(w, a, Q, Da, Db);
+    chunk_scales(w, Q, sa, sb);
+    const float fa = (float)(sa * Da);
+    const float fb = (float)(sb * Db);
+    return f16_bits_to_f32(w.d) * (a.da * fa + a.db * fb);
+}
+
+// Sum over the 64 lanes of a wave; every lane returns the same value.
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v += __shfl_xor(v, 32);
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 8);
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 1);
+    return v;
+}
+
+}  // namespace q6k

@@ -1,0 +1,156 @@
+"""The C ABI on the CPU: exported symbols, argument validation, sizes, host repack.
+
+No test here queues device work: every call with device pointers is given an
+argument that validation rejects before any HIP call is made.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import q6ksynth
+import quantized_decode_gemv_amd as q
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "q6kdpl.h")
+E_SHAPE, E_NULL, E_ALIGN, E_ALIAS = -1, -2, -3, -4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^[a-z_][\w \*]*?\b(\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_boundary():
+    names = set(declared_functions())
+    for n in ["repack_q6k_dpl", "rmsnorm_quant_q8", "mmvq_q6k_q8", "quant_q8",
+              "repack_q6k_dpl_host", "unpack_q6k_dpl_host", "mmvq_q6k_q8_subdots",
+              "q6k_strerror", "q6k_dpl_row_stride", "q8_plane_bytes"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    dll = ctypes.CDLL(q.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(dll, n)]
+    assert not missing, missing
+
+
+def test_version_and_errors_text():
+    assert "gfx950" in q.q6k_version()
+    for code in (0, -1, -2, -3, -4, -5, -99):
+        assert q.lib().q6k_strerror(code)
+
+
+@pytest.mark.parametrize("nbe", [1, 4, 20, 54, 74, 96, 97, 200, 4096])
+def test_sizes_match_oracle(nbe):
+    K = 256 * nbe
+    assert q.q6k_dpl_row_stride(K) == oracle.row_stride(oracle.DPL, K)
+    assert q.q6k_dpl_bytes(7, K) == 7 * oracle.row_stride(oracle.DPL, K)
+    assert q.q6k_raw_bytes(7, K) == 7 * 210 * nbe
+    assert q.q8_plane_bytes(K, 3) == 3 * K + 3 * (K // 32) * 2
+
+
+@pytest.mark.parametrize("K", [0, -256, 100, 255, 257, 256 * 4097])
+def test_bad_K_sizes_are_zero(K):
+    assert q.q6k_dpl_row_stride(K) == 0 and q.q6k_dpl_bytes(1, K) == 0
+
+
+def test_bad_sizes_are_zero():
+    assert q.q6k_dpl_bytes(0, 256) == 0 and q.q6k_dpl_bytes(-1, 256) == 0
+    assert q.q8_plane_bytes(48, 1) == 0 and q.q8_plane_bytes(64, 0) == 0
+    assert q.q8_plane_bytes(64, 257) == 0 and q.q8_plane_bytes(64, 256) == 256 * 68
+
+
+@pytest.mark.parametrize("N,K", [(1, 256), (5, 5120), (3, 18944), (2, 256 * 97)])
+def test_host_repack_matches_oracle_and_round_trips(N, K):
+    raw = q6ksynth.raw_q6k(N, K, seed=N + K)
+    dpl = np.full(q.q6k_dpl_bytes(N, K), 0xEE, np.uint8)   # pad bytes must be overwritten
+    q.repack_q6k_dpl_host(raw, dpl, N, K)
+    assert np.array_equal(dpl, oracle.repack_dpl(raw, N, K))
+    back = np.zeros_like(raw)
+    q.unpack_q6k_dpl_host(dpl, back, N, K)
+    assert np.array_equal(back, raw)
+
+
+def test_host_repack_rejects_overlap_and_null():
+    buf = np.zeros(4096, np.uint8)
+    with pytest.raises(q.Q6kError) as e:
+        q.repack_q6k_dpl_host(buf, buf.ctypes.data + 16, 1, 256)
+    assert e.value.code == E_ALIAS
+    with pytest.raises(q.Q6kError) as e:
+        q.repack_q6k_dpl_host(None, buf, 1, 256)
+    assert e.value.code == E_NULL
+
+
+# Fake, never-dereferenced device addresses (validation rejects before any HIP call).
+A, B, C, D = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+def _code(fn, *args):
+    with pytest.raises(q.Q6kError) as e:
+        fn(*args)
+    return e.value.code
+
+
+@pytest.mark.parametrize("N,K,nt", [(0, 256, 1), (-3, 256, 1), (1, 0, 1), (1, 255, 1),
+                                    (1, 288, 1), (1, 256, 0), (1, 256, 257),
+                                    (1, 256 * 4097, 1), (2 ** 30 + 1, 256, 1)])
+def test_mmvq_rejects_bad_shapes(N, K, nt):
+    assert _code(q.mmvq_q6k_q8, A, B, C, N, K, nt, 0) == E_SHAPE
+    assert _code(q.mmvq_q6k_q8_subdots, A, B, C, N, K, nt, 0) == E_SHAPE
+
+
+def test_mmvq_rejects_null_misaligned_and_aliased():
+    assert _code(q.mmvq_q6k_q8, None, B, C, 4, 256, 1, 0) == E_NULL
+    assert _code(q.mmvq_q6k_q8, A, None, C, 4, 256, 1, 0) == E_NULL
+    assert _code(q.mmvq_q6k_q8, A, B, None, 4, 256, 1, 0) == E_NULL
+    assert _code(q.mmvq_q6k_q8, A + 8, B, C, 4, 256, 1, 0) == E_ALIGN
+    assert _code(q.mmvq_q6k_q8, A, B + 4, C, 4, 256, 1, 0) == E_ALIGN
+    assert _code(q.mmvq_q6k_q8, A, B, C + 2, 4, 256, 1, 0) == E_ALIGN
+    # y overlapping the weights or the q8 plane
+    assert _code(q.mmvq_q6k_q8, A, B, A + 16, 4, 256, 1, 0) == E_ALIAS
+    assert _code(q.mmvq_q6k_q8, A, B, B + 32, 4, 256, 1, 0) == E_ALIAS
+    assert _code(q.mmvq_q6k_q8, A, B, A - 16, 8, 256, 1, 0) == E_ALIAS
+    assert _code(q.mmvq_q6k_q8_subdots, A, B, B, 4, 256, 1, 0) == E_ALIAS
+
+
+def test_producers_reject_bad_arguments():
+    assert _code(q.quant_q8, A, B, 48, 1, 0) == E_SHAPE
+    assert _code(q.quant_q8, A, B, 64, 0, 0) == E_SHAPE
+    assert _code(q.quant_q8, None, B, 64, 1, 0) == E_NULL
+    assert _code(q.quant_q8, A + 4, B, 64, 1, 0) == E_ALIGN
+    assert _code(q.quant_q8, A, A + 64, 64, 1, 0) == E_ALIAS
+    assert _code(q.rmsnorm_quant_q8, A, B, 1e-6, C, D, 40, 1, 0) == E_SHAPE
+    assert _code(q.rmsnorm_quant_q8, A, None, 1e-6, C, D, 64, 1, 0) == E_NULL
+    assert _code(q.rmsnorm_quant_q8, A, B, 1e-6, C + 8, D, 64, 1, 0) == E_ALIGN
+    assert _code(q.rmsnorm_quant_q8, A, B, 1e-6, A, D, 64, 1, 0) == E_ALIAS
+    assert _code(q.rmsnorm_quant_q8, A, B, 1e-6, C, C + 16, 64, 1, 0) == E_ALIAS
+    assert _code(q.rmsnorm_quant_q8, A, B, 1e-6, C, B, 64, 1, 0) == E_ALIAS
+
+
+def test_device_repack_rejects_bad_arguments():
+    assert _code(q.repack_q6k_dpl, A, B, 1, 100, 0) == E_SHAPE
+    assert _code(q.repack_q6k_dpl, A, None, 1, 256, 0) == E_NULL
+    assert _code(q.repack_q6k_dpl, A, B + 1, 1, 256, 0) == E_ALIGN
+    assert _code(q.repack_q6k_dpl, A, A + 64, 1, 256, 0) == E_ALIAS
+
+
+@pytest.mark.parametrize("nbe", list(range(1, 121)) + [200, 592, 4096])
+@pytest.mark.parametrize("nt", [1, 2, 4, 5, 9])
+def test_plan_covers_every_row_length(nbe, nt):
+    # every nbe reaches a kernel whose chunk count per lane covers the whole row
+    p = q.mmvq_plan(1000, 256 * nbe, nt, 256)
+    assert p["cpl"] * 64 >= 8 * nbe > (p["cpl"] - 1) * 64
+    assert p["unrolled"] == (p["cpl"] <= 12)
+    assert p["launches"] == -(-nt // 4)
+    assert p["grid"] >= 1
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 63, 64, 65, 4096, 152064])
+def test_plan_grid_never_exceeds_rows(N):
+    p = q.mmvq_plan(N, 5120, 1, 256)
+    assert 1 <= p["grid"] * 4 < N + 4 or p["grid"] == 256 * 16 // 4

@@ -1,0 +1,150 @@
+"""GPU parity: exact sub-block dots and the GEMV against the oracle, on every
+workload (full size, every output compared) plus dispatch edges."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import q6ksynth
+import quantized_decode_gemv_amd as q
+from gpu_util import (DEV, check_plane_vs_oracle_chain, check_y, dev_f32, dpl_from_raw,
+                      make_plane, oracle_threads, q8_plane, run_mmvq, say, split_plane)
+from q6k_build import onehot_probe
+
+pytestmark = pytest.mark.gpu
+
+
+def _chain(w: q6ksynth.Workload, nt: int):
+    """The workload's whole path on the GPU (device repack, its producer, the GEMV)
+    and on the oracle (repack-free raw rows, producer, GEMV), from the same seeds."""
+    raw = q6ksynth.weights(w)
+    dpl = dpl_from_raw(raw, w.N, w.K)
+    x = q6ksynth.activations(w, nt)
+    plane = q8_plane(w.K, nt)
+    if w.producer == "rmsnorm":
+        g = q6ksynth.gamma(w.K, q6ksynth.gamma_seed(w))
+        yd = torch.empty((nt, w.K), dtype=torch.float32, device=DEV)
+        q.rmsnorm_quant_q8(dev_f32(x), dev_f32(g), q6ksynth.RMS_EPS, yd, plane, w.K, nt)
+        x_or = oracle.rmsnorm(x, g, q6ksynth.RMS_EPS)
+        x_gpu = yd.cpu().numpy()
+    else:
+        q.quant_q8(dev_f32(x), plane, w.K, nt)
+        x_or = x_gpu = x
+    qs_or, d_or = oracle.quant_q8(x_or)
+    return raw, dpl, plane, x_gpu, x_or, qs_or, d_or
+
+
+@pytest.mark.parametrize("name,nt", [("tiny", 1), ("attn_v", 1), ("ffn_down", 1), ("tall_k", 1),
+                                     ("lm_head", 1), ("lm_head", 4)])
+def test_workload_full_parity(name, nt):
+    """Every output of every workload at full size. The GEMV is checked on the
+    oracle's q8 plane (both sides consume identical inputs); the GPU's own chain
+    (producer -> GEMV) is checked against the oracle chain when its q8 plane is
+    identical to the oracle's, which the producer test bounds block by block."""
+    w = q6ksynth.WORKLOADS[name]
+    say(f"workload {name} N={w.N} K={w.K} nt={nt}")
+    raw, dpl, plane, x_gpu, x_or, qs_or, d_or = _chain(w, nt)
+    y_or, A = oracle.mmvq(oracle.RAW, raw, w.N, w.K, qs_or, d_or, nthreads=oracle_threads())
+    y = run_mmvq(dpl, make_plane(qs_or, d_or), w.N, w.K, nt)
+    worst = check_y(y, y_or, A, name)
+    say(f"  GEMV on the oracle's q8: max err/A = {worst:.3e}")
+    qs, d = split_plane(plane, w.K, nt)
+    rep = check_plane_vs_oracle_chain(x_gpu, x_or, qs, d, qs_or, d_or, name)
+    say(f"  producer plane vs oracle chain: {rep}")
+    if rep["codes_differ"] == 0 and np.array_equal(d, d_or):
+        y_chain = run_mmvq(dpl, plane, w.N, w.K, nt)
+        check_y(y_chain, y_or, A, name + " chain")
+        assert np.array_equal(y_chain, y)
+    if name == "lm_head":
+        for t in range(nt):
+            top = np.argsort(y_or[t])[-2:]
+            margin = y_or[t, top[1]] - y_or[t, top[0]]
+            g = int(np.argmax(y[t]))
+            ok = g == top[1] or (margin <= 2 * 1e-5 * A[t, top].max() and g == top[0])
+            say(f"  token {t}: argmax gpu {g} oracle {top[1]} margin {margin:.4g}")
+            assert ok
+
+
+@pytest.mark.parametrize("N,K,nt", [(64, 1024, 1), (1024, 5120, 1), (37, 13824, 2),
+                                    (5, 18944, 3), (3, 256 * 97, 1), (2, 256 * 200, 5)])
+def test_subdots_bit_exact(N, K, nt):
+    say(f"subdots N={N} K={K} nt={nt}")
+    raw = q6ksynth.raw_q6k(N, K, seed=N * 7 + nt)
+    dpl = dpl_from_raw(raw, N, K)
+    x = np.stack([q6ksynth.activation("swiglu", K, 900 + c) for c in range(nt)])
+    qs, d = oracle.quant_q8(x)
+    plane = make_plane(qs, d)
+    dots = torch.zeros((nt, N, K // 16), dtype=torch.int32, device=DEV)
+    q.mmvq_q6k_q8_subdots(dpl, plane, dots, N, K, nt)
+    torch.cuda.synchronize()
+    assert np.array_equal(dots.cpu().numpy(), oracle.subdots(oracle.RAW, raw, N, K, qs))
+
+
+# chunks per lane change at nbe = 8k -> 8k+1; the unrolled/generic switch is at
+# nbe 96 -> 97; activation hoisting switches with nt * chunks-per-lane <= 6.
+EDGE_NBE = sorted({1, 2, 3, 7} | {8 * k for k in range(1, 13)} | {8 * k + 1 for k in range(0, 13)}
+                  | {100, 128, 200})
+
+
+@pytest.mark.parametrize("nbe", EDGE_NBE)
+@pytest.mark.parametrize("nt", [1, 2, 3, 4, 5])
+def test_dispatch_edges_random(nbe, nt):
+    K, N = 256 * nbe, 67
+    raw = q6ksynth.raw_q6k(N, K, seed=nbe * 10 + nt)
+    dpl = dpl_from_raw(raw, N, K)
+    x = np.stack([q6ksynth.activation("outlier", K, 1000 + c) for c in range(nt)])
+    qs, d = oracle.quant_q8(x)
+    y = run_mmvq(dpl, make_plane(qs, d), N, K, nt)
+    y_or, A = oracle.mmvq(oracle.RAW, raw, N, K, qs, d)
+    check_y(y, y_or, A, f"nbe={nbe} nt={nt}")
+
+
+@pytest.mark.parametrize("q0", [0, 1, 31, 33, 63])
+@pytest.mark.parametrize("nbe,block", [(1, 0), (4, 3)])
+def test_onehot_diagonal(q0, nbe, block):
+    raw, qs, d16, expect = onehot_probe(q0, nbe=nbe, block=block)
+    K = 256 * nbe
+    y = run_mmvq(dpl_from_raw(raw, 256, K), make_plane(qs, d16), 256, K, 256)
+    assert np.array_equal(y, expect.astype(np.float32))
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 63, 64, 65, 255, 256, 257, 4097])
+def test_row_counts(N):
+    K, nt = 5120, 2
+    raw = q6ksynth.raw_q6k(N, K, seed=N)
+    x = np.stack([q6ksynth.activation("normal", K, 1100 + c) for c in range(nt)])
+    qs, d = oracle.quant_q8(x)
+    y = run_mmvq(dpl_from_raw(raw, N, K), make_plane(qs, d), N, K, nt)
+    y_or, A = oracle.mmvq(oracle.RAW, raw, N, K, qs, d)
+    check_y(y, y_or, A, f"N={N}")
+
+
+def test_zero_scale_rows_are_exactly_zero():
+    N, K, nt = 40, 5120, 1
+    raw = q6ksynth.raw_q6k(N, K, seed=1)
+    blocks = raw.reshape(N, K // 256, 210)
+    blocks[::3, :, 208:210] = 0                      # every third row: d = 0
+    x = q6ksynth.activation("normal", K, 5)[None]
+    qs, d = oracle.quant_q8(x)
+    y = run_mmvq(dpl_from_raw(raw, N, K), make_plane(qs, d), N, K, 1)
+    assert np.all(y[0, ::3] == 0)
+    y_or, A = oracle.mmvq(oracle.RAW, raw, N, K, qs, d)
+    check_y(y, y_or, A, "zero-scale rows")
+
+
+def test_side_stream_and_repeat_calls_agree():
+    N, K, nt = 2048, 5120, 1
+    raw = q6ksynth.raw_q6k(N, K, seed=2)
+    dpl = dpl_from_raw(raw, N, K)
+    x = q6ksynth.activation("outlier", K, 6)[None]
+    qs, d = oracle.quant_q8(x)
+    plane = make_plane(qs, d)
+    y1 = run_mmvq(dpl, plane, N, K, nt)
+    s = torch.cuda.Stream()
+    y2 = torch.empty((nt, N), dtype=torch.float32, device=DEV)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            q.mmvq_q6k_q8(dpl, plane, y2, N, K, nt)
+    s.synchronize()
+    assert np.array_equal(y1, y2.cpu().numpy())      # same kernel, same order: bitwise
