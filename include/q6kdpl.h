@@ -133,11 +133,12 @@ int mmvq_q6k_q8_subdots(const void *w_dpl, const void *q8, int32_t *dots, int64_
                         int nt, void *stream);
 
 /* Diagnostics: how mmvq_q6k_q8 runs a shape on a device with num_cu compute units.
- * out5[0] = workgroups per launch (256 threads each), out5[1] = low-bit chunks per
- * lane per row, out5[2] = 1 for a fixed-length kernel (0: the generic stepping
- * kernel), out5[3] = 1 when activation operands stay in registers across rows,
- * out5[4] = launches (one per group of up to 4 token columns). Host only. */
-int q6k_mmvq_plan(int64_t N, int64_t K, int nt, int num_cu, int32_t *out5);
+ * out6[0] = workgroups per launch (256 threads each), out6[1] = low-bit chunks per
+ * lane per row, out6[2] = 1 for a fixed-length kernel (0: the generic stepping
+ * kernel), out6[3] = 1 when activation operands stay in registers across rows,
+ * out6[4] = launches (one per group of up to 4 token columns), out6[5] = rows in
+ * flight per wave. Host only. */
+int q6k_mmvq_plan(int64_t N, int64_t K, int nt, int num_cu, int32_t *out6);
 
 #ifdef __cplusplus
 }

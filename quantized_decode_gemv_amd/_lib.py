@@ -180,7 +180,7 @@ def mmvq_q6k_q8_subdots(w_dpl, q8, dots, N: int, K: int, nt: int, stream=None) -
 
 
 def mmvq_plan(N: int, K: int, nt: int, num_cu: int) -> dict:
-    out = (ctypes.c_int32 * 5)()
+    out = (ctypes.c_int32 * 6)()
     _call("q6k_mmvq_plan", N, K, nt, num_cu, ctypes.addressof(out))
     return dict(grid=out[0], cpl=out[1], unrolled=bool(out[2]), hoist=bool(out[3]),
-                launches=out[4])
+                launches=out[4], depth=out[5])

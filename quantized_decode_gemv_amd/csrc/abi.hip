@@ -214,18 +214,19 @@ int mmvq_q6k_q8_subdots(const void *w_dpl, const void *q8, int32_t *dots, int64_
                                         nt, cu, (hipStream_t)stream));
 }
 
-int q6k_mmvq_plan(int64_t N, int64_t K, int nt, int num_cu, int32_t *out5)
+int q6k_mmvq_plan(int64_t N, int64_t K, int nt, int num_cu, int32_t *out6)
 {
     if (!weight_shape_ok(N, K) || !act_shape_ok(K, nt) || num_cu < 1)
         return Q6K_E_SHAPE;
-    if (!out5)
+    if (!out6)
         return Q6K_E_NULL;
     const q6k::MmvqPlan p = q6k::plan_mmvq(N, K, nt, num_cu);
-    out5[0] = (int32_t)p.grid;
-    out5[1] = p.cpl;
-    out5[2] = p.unrolled;
-    out5[3] = p.hoist;
-    out5[4] = p.launches;
+    out6[0] = (int32_t)p.grid;
+    out6[1] = p.cpl;
+    out6[2] = p.unrolled;
+    out6[3] = p.hoist;
+    out6[4] = p.launches;
+    out6[5] = p.depth;
     return Q6K_OK;
 }
 

@@ -16,6 +16,7 @@ struct MmvqPlan {
     bool unrolled = false;  // a fixed-CPL kernel (else the generic stepping kernel)
     bool hoist = false;     // activation operands held in registers across rows
     int launches = 0;       // one launch per group of up to 4 token columns
+    int depth = 1;          // rows in flight per wave
 };
 
 MmvqPlan plan_mmvq(int64_t N, int64_t K, int nt, int num_cu);

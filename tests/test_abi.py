@@ -147,10 +147,12 @@ def test_plan_covers_every_row_length(nbe, nt):
     assert p["cpl"] * 64 >= 8 * nbe > (p["cpl"] - 1) * 64
     assert p["unrolled"] == (p["cpl"] <= 12)
     assert p["launches"] == -(-nt // 4)
-    assert p["grid"] >= 1
+    assert p["grid"] >= 1 and p["depth"] in (1, 2, 3)
 
 
-@pytest.mark.parametrize("N", [1, 2, 3, 63, 64, 65, 4096, 152064])
-def test_plan_grid_never_exceeds_rows(N):
-    p = q.mmvq_plan(N, 5120, 1, 256)
-    assert 1 <= p["grid"] * 4 < N + 4 or p["grid"] == 256 * 16 // 4
+@pytest.mark.parametrize("N", [1, 2, 3, 63, 64, 65, 1023, 1024, 1025, 4096, 152064])
+@pytest.mark.parametrize("nt", [1, 2, 4])
+def test_plan_grid_is_whole_cus_or_one_wave_per_row(N, nt):
+    p = q.mmvq_plan(N, 5120, nt, 256)
+    waves_needed = -(-N // 4)
+    assert p["grid"] == waves_needed or (p["grid"] % 256 == 0 and p["grid"] < waves_needed)
