@@ -18,8 +18,9 @@
 //    keep the default policy (each 64-byte line of them is touched by three load
 //    instructions of the same row);
 //  - lanes past the row's last chunk load a duplicate of the last chunk and
-//    contribute exactly 0, and a wave's look-ahead past the last row re-requests its
-//    current row, so loads are branch-free and their waits are counted exactly;
+//    contribute exactly 0, and a wave's look-ahead past the last row uses an empty
+//    descriptor (its loads return zeros without touching memory), so loads are
+//    branch-free and their waits are counted exactly;
 //  - DEPTH rows are in flight per wave: the next rows' loads are issued before the
 //    current row's arithmetic (scheduling barriers keep the compiler from sinking
 //    them), so a wave never idles with nothing requested;
@@ -66,11 +67,13 @@ __device__ __forceinline__ ChunkOffs chunk_offsets(uint32_t Q, uint32_t nbe)
     return o;
 }
 
+// Descriptor of one row; extent 0 for a look-ahead row past the end, whose loads
+// then return zeros without a memory request.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_desc(const uint8_t *w, uint32_t row,
-                                                           uint32_t stride)
+                                                           uint32_t stride, bool real = true)
 {
     return __builtin_amdgcn_make_buffer_rsrc((void *)(w + (size_t)row * stride), (short)0,
-                                             (int)stride, DESC_WORD3);
+                                             real ? (int)stride : 0, DESC_WORD3);
 }
 
 __device__ __forceinline__ ChunkW load_chunk(__amdgpu_buffer_rsrc_t r, const ChunkOffs &o)
@@ -142,9 +145,11 @@ __device__ __forceinline__ void lane_init(LaneState<NT, CPL, HOIST> &st, uint32_
 
 template <int NT, int CPL, bool HOIST>
 __device__ __forceinline__ void load_row(ChunkW (&dst)[CPL], const uint8_t *w, uint32_t row,
-                                         uint32_t stride, const LaneState<NT, CPL, HOIST> &st)
+                                         uint32_t N, uint32_t stride,
+                                         const LaneState<NT, CPL, HOIST> &st)
 {
-    const __amdgpu_buffer_rsrc_t r = row_desc(w, row, stride);
+    const bool real = row < N;
+    const __amdgpu_buffer_rsrc_t r = row_desc(w, real ? row : 0u, stride, real);
 #pragma unroll
     for (int i = 0; i < CPL; ++i)
         dst[i] = load_chunk(r, st.off[i]);
@@ -198,29 +203,28 @@ __global__ __launch_bounds__(WG) void mmvq_rows(const uint8_t *__restrict__ w,
     lane_init(st, lane, nbe, qs, d8, K);
     if (wave >= N)
         return;
-    // a row past the end is replaced by the wave's current row (a duplicate of data
-    // it has just requested, never reduced), keeping every load unconditional
-#define Q6K_ROW(r) ((r) < N ? (r) : row)
+    // look-ahead rows past the end get an empty descriptor (load_row), so every load
+    // stays unconditional and their results are never reduced
 #define Q6K_FINISH(BUF, ROW) finish_row<NT, CPL, HOIST>(BUF, st, qs, d8, K, y, ldy, ROW, lane)
     if constexpr (DEPTH == 1) {
         ChunkW A[CPL];
         for (uint32_t row = wave; row < N; row += nw) {
-            load_row(A, w, row, stride, st);
+            load_row(A, w, row, N, stride, st);
             Q6K_FINISH(A, row);
         }
     } else if constexpr (DEPTH == 2) {
         ChunkW A[CPL], B[CPL];
         uint32_t row = wave;
-        load_row(A, w, row, stride, st);
+        load_row(A, w, row, N, stride, st);
         for (;;) {
             const uint32_t r1 = row + nw;
-            load_row(B, w, Q6K_ROW(r1), stride, st);
+            load_row(B, w, r1, N, stride, st);
             __builtin_amdgcn_sched_barrier(0);
             Q6K_FINISH(A, row);
             if (r1 >= N)
                 break;
             const uint32_t r2 = r1 + nw;
-            load_row(A, w, Q6K_ROW(r2), stride, st);
+            load_row(A, w, r2, N, stride, st);
             __builtin_amdgcn_sched_barrier(0);
             Q6K_FINISH(B, r1);
             if (r2 >= N)
@@ -230,21 +234,21 @@ __global__ __launch_bounds__(WG) void mmvq_rows(const uint8_t *__restrict__ w,
     } else {
         ChunkW A[CPL], B[CPL], Cb[CPL];
         uint32_t row = wave;
-        load_row(A, w, row, stride, st);
-        load_row(B, w, Q6K_ROW(row + nw), stride, st);
+        load_row(A, w, row, N, stride, st);
+        load_row(B, w, row + nw, N, stride, st);
         for (;;) {
             const uint32_t r1 = row + nw, r2 = r1 + nw, r3 = r2 + nw;
-            load_row(Cb, w, Q6K_ROW(r2), stride, st);
+            load_row(Cb, w, r2, N, stride, st);
             __builtin_amdgcn_sched_barrier(0);
             Q6K_FINISH(A, row);
             if (r1 >= N)
                 break;
-            load_row(A, w, Q6K_ROW(r3), stride, st);
+            load_row(A, w, r3, N, stride, st);
             __builtin_amdgcn_sched_barrier(0);
             Q6K_FINISH(B, r1);
             if (r2 >= N)
                 break;
-            load_row(B, w, Q6K_ROW(r3 + nw), stride, st);
+            load_row(B, w, r3 + nw, N, stride, st);
             __builtin_amdgcn_sched_barrier(0);
             Q6K_FINISH(Cb, r2);
             if (r3 >= N)
@@ -252,7 +256,6 @@ __global__ __launch_bounds__(WG) void mmvq_rows(const uint8_t *__restrict__ w,
             row = r3;
         }
     }
-#undef Q6K_ROW
 #undef Q6K_FINISH
 }
 

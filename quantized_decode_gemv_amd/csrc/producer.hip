@@ -9,9 +9,10 @@
 // and its block's amax (max is exact under any association).
 //
 // Thread geometry: a lane holds 4 consecutive values (one float4), 8 consecutive
-// lanes hold one 32-value block, and the block's amax is an xor-butterfly max over
-// those 8 lanes. Every lane of a wave runs the butterfly; lanes past the end carry
-// zeros and store nothing, so no lane leaves before a cross-lane step.
+// lanes hold one 32-value block, and the block's amax is a DPP max over those 8
+// lanes (pairs, quads, then mirrored half-rows). Every lane of a wave runs it;
+// lanes past the end carry zeros and store nothing, so no lane leaves before a
+// cross-lane step.
 
 #include "q6k_internal.h"
 
@@ -30,13 +31,20 @@ __device__ __forceinline__ int q_of(float v, float di)
     return q < -128 ? -128 : (q > 127 ? 127 : q);
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v)
+{
+    return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                        0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false)));
+}
+
 // All 64 lanes must call this together; lanes 8m..8m+7 form one block.
 __device__ __forceinline__ Q8Out quant_group8(float4 v)
 {
     float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    m = fmaxf(m, __shfl_xor(m, 4));
-    m = fmaxf(m, __shfl_xor(m, 2));
-    m = fmaxf(m, __shfl_xor(m, 1));
+    m = dpp_max<0xB1>(m);    // quad_perm [1,0,3,2]: pairs
+    m = dpp_max<0x4E>(m);    // quad_perm [2,3,0,1]: quads
+    m = dpp_max<0x141>(m);   // row_half_mirror: the two quads of each 8 lanes
     const float d = m / 127.0f;
     const float di = (d != 0.0f) ? 1.0f / d : 0.0f;
     Q8Out o;
@@ -66,42 +74,102 @@ __global__ __launch_bounds__(QWG) void quant_q8_kernel(const float4 *__restrict_
     }
 }
 
-// One workgroup per token row. Pass 1: fp64 sum of squares (each x^2 is exact in
-// fp64), reduced in a fixed order; r = f32(1 / sqrt(mean + eps)). Pass 2: y = (x*r)*g
-// in f32, stored, and quantized from registers by the q8 body (the same values the
-// row holds in memory, so the bytes equal quant_q8 applied to y).
+__device__ __forceinline__ double block_sum_f64(double v, double *part, int nwaves)
+{
+    v += __shfl_xor(v, 32);
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 8);
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 1);
+    if ((threadIdx.x & 63u) == 0)
+        part[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double tot = 0.0;
+    for (int i = 0; i < nwaves; ++i)    // every thread adds in the same order
+        tot += part[i];
+    return tot;
+}
+
+__device__ __forceinline__ float4 rms_scale(float4 x, float4 g, float r)
+{
+    return make_float4((x.x * r) * g.x, (x.y * r) * g.y, (x.z * r) * g.z, (x.w * r) * g.w);
+}
+
+__device__ __forceinline__ double sq_sum(float4 v)
+{
+    double s = (double)v.x * (double)v.x;
+    s += (double)v.y * (double)v.y;
+    s += (double)v.z * (double)v.z;
+    s += (double)v.w * (double)v.w;
+    return s;
+}
+
+// One workgroup per token row, the whole row held in registers (VPT float4 per
+// thread, K/4 <= BS*VPT). The sum of squares is fp64 (each x^2 is exact in fp64)
+// in a fixed reduction order; r = f32(1 / sqrt(mean + eps)); y = (x*r)*g in f32 is
+// stored and quantized from the same registers (the bytes equal quant_q8 applied
+// to y).
+template <int BS, int VPT>
+__global__ __launch_bounds__(BS) void rmsnorm_quant_regs(const float4 *__restrict__ x,
+                                                         const float4 *__restrict__ g,
+                                                         float eps, float4 *__restrict__ y,
+                                                         uint32_t *__restrict__ qs,
+                                                         uint16_t *__restrict__ d8, uint32_t K)
+{
+    const uint32_t t = blockIdx.x;
+    const uint32_t K4 = K / 4u;
+    const float4 *xr = x + (size_t)t * K4;
+    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 xv[VPT], gv[VPT];
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const uint32_t f = threadIdx.x + v * BS;
+        xv[v] = f < K4 ? xr[f] : zero;
+        gv[v] = f < K4 ? g[f] : zero;
+    }
+    double ss = 0.0;
+#pragma unroll
+    for (int v = 0; v < VPT; ++v)
+        ss += sq_sum(xv[v]);
+    __shared__ double part[BS / 64];
+    const double tot = block_sum_f64(ss, part, BS / 64);
+    const float r = (float)(1.0 / sqrt(tot / (double)K + (double)eps));
+
+    float4 *yr = y + (size_t)t * K4;
+    uint32_t *qr = qs + (size_t)t * K4;
+    uint16_t *dr = d8 + (size_t)t * (K / 32u);
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const uint32_t f = threadIdx.x + v * BS;
+        const bool live = f < K4;
+        const float4 yv = rms_scale(xv[v], gv[v], r);
+        const Q8Out o = quant_group8(yv);
+        if (live) {
+            yr[f] = yv;
+            qr[f] = o.packed;
+            if ((f & 7u) == 0)
+                dr[f >> 3] = o.d16;
+        }
+    }
+}
+
+// Any row length: the same computation, walking the row twice from memory.
 template <int BS>
-__global__ __launch_bounds__(BS) void rmsnorm_quant_kernel(const float4 *__restrict__ x,
-                                                           const float4 *__restrict__ g,
-                                                           float eps, float4 *__restrict__ y,
-                                                           uint32_t *__restrict__ qs,
-                                                           uint16_t *__restrict__ d8, uint32_t K)
+__global__ __launch_bounds__(BS) void rmsnorm_quant_loop(const float4 *__restrict__ x,
+                                                         const float4 *__restrict__ g,
+                                                         float eps, float4 *__restrict__ y,
+                                                         uint32_t *__restrict__ qs,
+                                                         uint16_t *__restrict__ d8, uint32_t K)
 {
     const uint32_t t = blockIdx.x;
     const uint32_t K4 = K / 4u;
     const float4 *xr = x + (size_t)t * K4;
     double ss = 0.0;
-    for (uint32_t f = threadIdx.x; f < K4; f += BS) {
-        const float4 v = xr[f];
-        ss += (double)v.x * (double)v.x;
-        ss += (double)v.y * (double)v.y;
-        ss += (double)v.z * (double)v.z;
-        ss += (double)v.w * (double)v.w;
-    }
-    ss += __shfl_xor(ss, 32);
-    ss += __shfl_xor(ss, 16);
-    ss += __shfl_xor(ss, 8);
-    ss += __shfl_xor(ss, 4);
-    ss += __shfl_xor(ss, 2);
-    ss += __shfl_xor(ss, 1);
+    for (uint32_t f = threadIdx.x; f < K4; f += BS)
+        ss += sq_sum(xr[f]);
     __shared__ double part[BS / 64];
-    if ((threadIdx.x & 63u) == 0)
-        part[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    double tot = 0.0;
-#pragma unroll
-    for (int i = 0; i < BS / 64; ++i)
-        tot += part[i];
+    const double tot = block_sum_f64(ss, part, BS / 64);
     const float r = (float)(1.0 / sqrt(tot / (double)K + (double)eps));
 
     float4 *yr = y + (size_t)t * K4;
@@ -111,18 +179,10 @@ __global__ __launch_bounds__(BS) void rmsnorm_quant_kernel(const float4 *__restr
     for (uint32_t it = 0; it < iters; ++it) {
         const uint32_t f = it * BS + threadIdx.x;
         const bool live = f < K4;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 yv = live ? rms_scale(xr[f], g[f], r) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const Q8Out o = quant_group8(yv);
         if (live) {
-            const float4 xv = xr[f];
-            const float4 gv = g[f];
-            v.x = (xv.x * r) * gv.x;
-            v.y = (xv.y * r) * gv.y;
-            v.z = (xv.z * r) * gv.z;
-            v.w = (xv.w * r) * gv.w;
-            yr[f] = v;
-        }
-        const Q8Out o = quant_group8(v);
-        if (live) {
+            yr[f] = yv;
             qr[f] = o.packed;
             if ((f & 7u) == 0)
                 dr[f >> 3] = o.d16;
@@ -154,12 +214,16 @@ hipError_t launch_rmsnorm_quant(const float *x, const float *gamma, float eps, f
     uint32_t Ku = (uint32_t)K;
     void *args[] = {(void *)&x4, (void *)&g4, (void *)&eps, (void *)&y4,
                     (void *)&qs, (void *)&d8, (void *)&Ku};
-    // 1024 threads for long rows so each lane holds few float4s; 256 otherwise.
-    if (K >= 8192)
-        return hipLaunchKernel((const void *)rmsnorm_quant_kernel<1024>, dim3(nt), dim3(1024),
-                               args, 0, s);
-    return hipLaunchKernel((const void *)rmsnorm_quant_kernel<256>, dim3(nt), dim3(256), args, 0,
-                           s);
+    const int64_t K4 = K / 4;
+    const void *kern;
+    int bs;
+    if (K4 <= 256 * 2) { kern = (const void *)rmsnorm_quant_regs<256, 2>; bs = 256; }
+    else if (K4 <= 256 * 4) { kern = (const void *)rmsnorm_quant_regs<256, 4>; bs = 256; }
+    else if (K4 <= 256 * 8) { kern = (const void *)rmsnorm_quant_regs<256, 8>; bs = 256; }
+    else if (K4 <= 1024 * 4) { kern = (const void *)rmsnorm_quant_regs<1024, 4>; bs = 1024; }
+    else if (K4 <= 1024 * 8) { kern = (const void *)rmsnorm_quant_regs<1024, 8>; bs = 1024; }
+    else { kern = (const void *)rmsnorm_quant_loop<1024>; bs = 1024; }
+    return hipLaunchKernel(kern, dim3(nt), dim3(bs), args, 0, s);
 }
 
 }  // namespace q6k

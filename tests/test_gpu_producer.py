@@ -75,7 +75,13 @@ def test_quant_q8_wide_dynamic_range():
     assert np.array_equal(qs, qs_o) and np.array_equal(d, d_o)
 
 
-@pytest.mark.parametrize("K", [256, 1024, 5120, 8192, 13824, 18944])
+# every register-resident variant's edge (K/4 = 512, 1024, 2048, 4096, 8192 float4s)
+# and the looping form past K = 32768
+RMS_K = [256, 1024, 2048, 2080, 4096, 4128, 5120, 8192, 8224, 13824, 16384, 16416, 18944,
+         32768, 32800, 40960]
+
+
+@pytest.mark.parametrize("K", RMS_K)
 @pytest.mark.parametrize("nt", [1, 4])
 def test_rmsnorm_quant_q8(K, nt):
     """y within the reading's tolerance (the reduction order is free); the q8 plane
