@@ -26,8 +26,8 @@
 //    them), so a wave never idles with nothing requested;
 //  - a lane's activation operands are the same for every row; they stay in
 //    registers (HOIST) when they fit, else they are re-read per row (cached);
-//  - a row ends with a DPP reduction inside each 16-lane row and four lane reads;
-//    lane 0 writes.
+//  - a row ends with one reduction for all its token columns (DPP inside each
+//    16-lane row, lane swaps across rows); lanes 0..NT-1 write the NT outputs.
 // The chunks per lane (CPL = ceil(8*nbe/64)) is a template parameter up to
 // MAX_CPL, so a row's loads are issued back to back; longer rows take the generic
 // kernel, which walks a row in runtime steps of 4 chunks per lane. Every kernel
@@ -90,28 +90,69 @@ __device__ __forceinline__ ChunkW load_chunk(__amdgpu_buffer_rsrc_t r, const Chu
     return w;
 }
 
-// Sum over a wave64. Inside each 16-lane row: pair, quad, half-row and row sums by
-// DPP; the four row sums are then read and added in a fixed order. Every call adds
-// in the same tree, so results are reproducible run to run.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                         0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_add(float v)
 {
-    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                   0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+    return v + dpp_mov<CTRL>(v);
 }
 
-__device__ __forceinline__ float wave_total(float v)
+// Sums over a wave64 of NT <= 4 per-lane values (one per token column). The
+// first steps transpose while they add: at the pair step a lane keeps the tokens
+// of its parity and hands the others to its partner, at the quad step likewise by
+// the second lane bit, so afterwards lane l carries only token (l & 3) (for NT = 2:
+// l & 1). Rotations by 4 and 8 lanes finish each 16-lane row; two lane-swaps add
+// the four rows. Lane l then holds the total of token (l & 3) (NT = 1: of the only
+// token). The adds always pair the same lanes in the same order, so results are
+// reproducible run to run.
+template <int NT>
+__device__ __forceinline__ float reduce_tokens(const float (&a)[NT], uint32_t lane)
 {
-    v = dpp_add<0xB1>(v);    // quad_perm [1,0,3,2]
-    v = dpp_add<0x4E>(v);    // quad_perm [2,3,0,1]
-    v = dpp_add<0x141>(v);   // row_half_mirror
-    v = dpp_add<0x140>(v);   // row_mirror
-    const int b = __builtin_bit_cast(int, v);
-    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
-    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
-    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
-    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
-    return (r0 + r1) + (r2 + r3);
+    static_assert(NT >= 1 && NT <= 4, "one to four token columns per reduction");
+    float v;
+    if constexpr (NT == 1) {
+        v = dpp_add<0xB1>(a[0]);                     // quad_perm [1,0,3,2]
+        v = dpp_add<0x4E>(v);                        // quad_perm [2,3,0,1]
+    } else {
+        const bool b0 = (lane & 1u) != 0;
+        if constexpr (NT == 2) {
+            v = (b0 ? a[1] : a[0]) + dpp_mov<0xB1>(b0 ? a[0] : a[1]);
+            v = dpp_add<0x4E>(v);
+        } else {
+            const bool b1 = (lane & 2u) != 0;
+            const float a2 = a[2], a3 = NT > 3 ? a[NT - 1] : 0.0f;
+            const float p = (b0 ? a[1] : a[0]) + dpp_mov<0xB1>(b0 ? a[0] : a[1]);
+            const float q = (b0 ? a3 : a2) + dpp_mov<0xB1>(b0 ? a2 : a3);
+            v = (b1 ? q : p) + dpp_mov<0x4E>(b1 ? p : q);
+        }
+    }
+    v = dpp_add<0x124>(v);                           // row_ror:4
+    v = dpp_add<0x128>(v);                           // row_ror:8
+    // (each swap's two results are copied into plain integers before their bit
+    // casts: a bit cast applied straight to an element of the returned pair reads
+    // element 0 for both)
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const unsigned h0 = h[0], h1 = h[1];
+    v = __builtin_bit_cast(float, h0) + __builtin_bit_cast(float, h1);
+    const unsigned u2 = __builtin_bit_cast(unsigned, v);
+    const auto r = __builtin_amdgcn_permlane16_swap(u2, u2, false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+
+// The lane that holds token t's total after reduce_tokens.
+template <int NT>
+__device__ __forceinline__ bool stores_token(uint32_t lane, uint32_t &t)
+{
+    t = NT == 1 ? 0u : lane;
+    return lane < (uint32_t)NT;
 }
 
 // Per-lane state that is the same for every row a wave visits.
@@ -167,25 +208,22 @@ __device__ __forceinline__ void finish_row(const ChunkW (&src)[CPL],
         acc[t] = 0.0f;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
+        const float d = st.live[i] ? f16_bits_to_f32(src[i].d) : 0.0f;   // 0 drops the chunk
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            float p;
             if constexpr (HOIST) {
-                p = chunk_partial(src[i], st.act[i][t], st.Q[i]);
+                acc[t] += chunk_partial_d(src[i], st.act[i][t], st.Q[i], d);
             } else {
                 const ChunkAct a =
                     load_act(qs + (size_t)t * K, d8 + (size_t)t * (K / 32), st.Q[i]);
-                p = chunk_partial(src[i], a, st.Q[i]);
+                acc[t] += chunk_partial_d(src[i], a, st.Q[i], d);
             }
-            acc[t] += st.live[i] ? p : 0.0f;
         }
     }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        const float s = wave_total(acc[t]);
-        if (lane == 0)
-            y[(size_t)t * ldy + row] = s;
-    }
+    const float s = reduce_tokens<NT>(acc, lane);
+    uint32_t t;
+    if (stores_token<NT>(lane, t))
+        y[(size_t)t * ldy + row] = s;
 }
 
 // Rows with at most MAX_CPL chunks per lane; DEPTH rows in flight per wave.
@@ -291,21 +329,19 @@ __global__ __launch_bounds__(WG) void mmvq_long(const uint8_t *__restrict__ w,
             }
 #pragma unroll
             for (int i = 0; i < STEP; ++i) {
+                const float d = live[i] ? f16_bits_to_f32(wt[i].d) : 0.0f;
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
                     const ChunkAct a =
                         load_act(qs + (size_t)t * K, d8 + (size_t)t * (K / 32), Qs[i]);
-                    const float p = chunk_partial(wt[i], a, Qs[i]);
-                    acc[t] += live[i] ? p : 0.0f;
+                    acc[t] += chunk_partial_d(wt[i], a, Qs[i], d);
                 }
             }
         }
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const float s = wave_total(acc[t]);
-            if (lane == 0)
-                y[(size_t)t * ldy + row] = s;
-        }
+        const float s = reduce_tokens<NT>(acc, lane);
+        uint32_t t;
+        if (stores_token<NT>(lane, t))
+            y[(size_t)t * ldy + row] = s;
     }
 }
 
@@ -359,7 +395,7 @@ RowsCfg rows_cfg(int nt, int cpl)
     const int work = nt * cpl;
     if (work <= 3)
         return {3, true, 1};
-    if (work <= 6)
+    if (work <= 6 || (cpl <= 3 && work <= 12))
         return {2, true, 2};
     return {1, false, 2};
 }
@@ -383,7 +419,7 @@ hipError_t launch_cpl(const RowsCfg &c, uint32_t grid, hipStream_t s, const uint
     if constexpr (NT * CPL <= 3) {
         if (c.depth == 3)
             return launch(mmvq_rows<NT, CPL, 3, true>, grid, s, w, qs, d8, y, N, nbe, stride, K, ldy);
-    } else if constexpr (NT * CPL <= 6) {
+    } else if constexpr (NT * CPL <= 6 || (CPL <= 3 && NT * CPL <= 12)) {
         if (c.depth == 2)
             return launch(mmvq_rows<NT, CPL, 2, true>, grid, s, w, qs, d8, y, N, nbe, stride, K, ldy);
     } else {

@@ -125,28 +125,24 @@ __device__ __forceinline__ void chunk_scales(const ChunkW &w, uint32_t Q, int &s
     sb = (int)(int8_t)(uint8_t)(w.sc.y >> bit);
 }
 
-// The chunk's contribution d * (d8a * sa*Da + d8b * sb*Db). sa*Da and sb*Db are
-// exact integers below 2^23, so their f32 conversion is exact.
-__device__ __forceinline__ float chunk_partial(const ChunkW &w, const ChunkAct &a, uint32_t Q)
+// The chunk's contribution d * (d8a * sa*Da + d8b * sb*Db), with d passed in (the
+// caller may zero it to drop the chunk). |sa| <= 128 and |D| <= 2^16 fit the 24-bit
+// multiplier, and sa*Da, sb*Db are exact integers below 2^23, so their f32
+// conversion is exact.
+__device__ __forceinline__ float chunk_partial_d(const ChunkW &w, const ChunkAct &a, uint32_t Q,
+                                                 float d)
 {
     int Da, Db, sa, sb;
     chunk_dots(w, a, Q, Da, Db);
     chunk_scales(w, Q, sa, sb);
-    const float fa = (float)(sa * Da);
-    const float fb = (float)(sb * Db);
-    return f16_bits_to_f32(w.d) * (a.da * fa + a.db * fb);
+    const float fa = (float)__mul24(sa, Da);
+    const float fb = (float)__mul24(sb, Db);
+    return d * (a.da * fa + a.db * fb);
 }
 
-// Sum over the 64 lanes of a wave; every lane returns the same value.
-__device__ __forceinline__ float wave_sum(float v)
+__device__ __forceinline__ float chunk_partial(const ChunkW &w, const ChunkAct &a, uint32_t Q)
 {
-    v += __shfl_xor(v, 32);
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 8);
-    v += __shfl_xor(v, 4);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 1);
-    return v;
+    return chunk_partial_d(w, a, Q, f16_bits_to_f32(w.d));
 }
 
 }  // namespace q6k
