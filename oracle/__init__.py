@@ -21,7 +21,7 @@ import numpy as np
 __all__ = [
     "RAW", "PAD224", "DPL", "build", "row_stride", "f16_to_f64", "f32_to_f16",
     "decode", "dequant", "repack_dpl", "unpack_dpl", "pad224", "quant_q8",
-    "rmsnorm", "subdots", "mmvq", "mmvq_exact",
+    "rmsnorm", "swiglu", "subdots", "mmvq", "mmvq_exact",
 ]
 
 RAW, PAD224, DPL = 0, 1, 2
@@ -67,6 +67,7 @@ def _load():
             "orc_pad224": (_INT, [_P, _P, _I64, _I64]),
             "orc_quant_q8": (_INT, [_P, _I64, _INT, _P, _P]),
             "orc_rmsnorm": (_INT, [_P, _P, ctypes.c_float, _I64, _INT, _P]),
+            "orc_swiglu": (_INT, [_P, _P, _I64, _INT, _P]),
             "orc_subdots": (_INT, [_INT, _P, _I64, _I64, _INT, _P, _P]),
             "orc_mmvq": (_INT, [_INT, _P, _I64, _I64, _INT, _P, _P, _P, _P, _INT]),
             "orc_mmvq_exact": (_INT, [_INT, _P, _I64, _I64, _INT, _P, _P, _P]),
@@ -169,6 +170,17 @@ def rmsnorm(x, gamma, eps: float) -> np.ndarray:
     assert gamma.shape == (K,)
     y = np.empty((nt, K), np.float32)
     _check(_load().orc_rmsnorm(_ptr(x), _ptr(gamma), float(eps), K, nt, _ptr(y)), "rmsnorm")
+    return y
+
+
+def swiglu(g, u) -> np.ndarray:
+    """g, u float32 [nt, K] -> y = silu(g) * u float32 [nt, K] (exact, rounded once)."""
+    g = np.ascontiguousarray(np.atleast_2d(g), dtype=np.float32)
+    u = np.ascontiguousarray(np.atleast_2d(u), dtype=np.float32)
+    assert g.shape == u.shape
+    nt, K = g.shape
+    y = np.empty((nt, K), np.float32)
+    _check(_load().orc_swiglu(_ptr(g), _ptr(u), K, nt, _ptr(y)), "swiglu")
     return y
 
 

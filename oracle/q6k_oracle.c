@@ -19,6 +19,10 @@
  *   [D3-5] "70 · D3-5 -- decode-alignment plan Stage 1: fused-producer decode
  *           A-quantize"
  *
+ * The SwiGLU producer (orc_swiglu) is the plain definition silu(g) * u, computed in
+ * fp64 and rounded once to f32; the pages' f32 body rounds at each step, so the
+ * HIP producer is compared to it within a few ulp (its last bits are not pinned).
+ *
  * Parity pins (tests/test_oracle_*.py): every function here is pinned by something
  * other than itself -- hand-worked addressing fixtures, closed forms, exact
  * integer sums, brute force on tiny inputs and the raw == padded == dpl invariant.
@@ -329,6 +333,20 @@ int orc_rmsnorm(const float *x, const float *gamma, float eps, int64_t K, int nt
             float xn = xr[k] * r;
             y[(int64_t)t * K + k] = xn * gamma[k];
         }
+    }
+    return ORC_OK;
+}
+
+/* SwiGLU of nt rows of K gate/up pairs: y = silu(g) * u = g / (1 + e^-g) * u
+ * ([D3-5] §3.2, the fused swiglu producer's body), the exact value rounded once
+ * to f32 (evaluated in fp64). */
+int orc_swiglu(const float *g, const float *u, int64_t K, int nt, float *y)
+{
+    if (K <= 0 || nt < 1)
+        return ORC_E_SHAPE;
+    for (int64_t i = 0; i < (int64_t)nt * K; i++) {
+        const double gd = (double)g[i];
+        y[i] = (float)(gd / (1.0 + exp(-gd)) * (double)u[i]);
     }
     return ORC_OK;
 }

@@ -120,3 +120,43 @@ def test_rmsnorm_eps_enters_inside_the_root():
     K = 32
     y = oracle.rmsnorm(np.ones((1, K), np.float32), np.ones(K, np.float32), 0.25)
     assert np.all(y == np.float32(1 / np.sqrt(1.25)))
+
+
+# --- SwiGLU (silu(g) * u) --------------------------------------------------------
+
+def test_swiglu_textbook_values():
+    # silu(0) = 0; silu(1) = 1/(1 + e^-1) = 0.7310585786300049 (sigma(1)); silu(-1) =
+    # -0.2689414213699951; at g = +-40 the logistic saturates: silu(40) = 40 in f32 and
+    # silu(-40) = -40 e^-40 / (1 + e^-40) = -1.6993e-16.
+    g = np.array([[0.0, 1.0, -1.0, 40.0, -40.0, 2.0]], np.float32)
+    u = np.ones_like(g)
+    y = oracle.swiglu(g, u)[0]
+    assert y[0] == 0.0
+    assert y[1] == np.float32(0.7310585786300049)
+    assert y[2] == np.float32(-0.2689414213699951)
+    assert y[3] == np.float32(40.0)
+    assert abs(y[4] - np.float32(-1.6993417021166355e-16)) <= np.spacing(np.float32(1.7e-16))
+    assert y[5] == np.float32(1.7615941559557649)   # 2 * sigma(2)
+
+
+def test_swiglu_odd_part_identity():
+    # silu(x) - silu(-x) = x exactly in real arithmetic; with one f32 rounding of each
+    # term the difference is within an ulp of each.
+    rng = np.random.default_rng(21)
+    g = rng.standard_normal((1, 4096)).astype(np.float32) * np.float32(4)
+    one = np.ones_like(g)
+    a = oracle.swiglu(g, one).astype(np.float64)
+    b = oracle.swiglu(-g, one).astype(np.float64)
+    tol = np.spacing(np.abs(a).astype(np.float32)) + np.spacing(np.abs(b).astype(np.float32))
+    assert np.all(np.abs((a - b) - g.astype(np.float64)) <= tol)
+
+
+def test_swiglu_is_linear_in_u_and_zero_rows():
+    rng = np.random.default_rng(22)
+    g = rng.standard_normal((2, 512)).astype(np.float32)
+    u = rng.standard_normal((2, 512)).astype(np.float32)
+    y1 = oracle.swiglu(g, u)
+    y2 = oracle.swiglu(g, u * np.float32(4))          # power-of-two scaling is exact
+    assert np.array_equal(y2, y1 * np.float32(4))
+    assert not oracle.swiglu(g, np.zeros_like(u)).any()
+    assert not oracle.swiglu(np.zeros_like(g), u).any()
