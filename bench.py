@@ -34,6 +34,8 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 PAGES_LM_HEAD_GBS = 250.0       # the pages' dpl lm_head content rate (GB10; context only)
 ROTATE_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mmvq_lm_head_traffic.txt")
+PRODUCER_NAMES = {"rmsnorm": "fused RMSNorm->q8", "swiglu": "fused SwiGLU->q8",
+                  "quant": "q8"}
 KERNEL_SOURCES = [os.path.join(ROOT, "quantized_decode_gemv_amd", "csrc", f)
                   for f in ("mmvq.hip", "q6k_unit.h")]
 
@@ -79,15 +81,19 @@ def copy_calib(steps: int) -> None:
                       "launches": steps}), flush=True)
 
 
-def cpu_baseline(w, raw, x, g, nt: int, budget_s: float = 20.0) -> dict:
-    """The oracle chain (RMSNorm, q8, GEMV) on the host over a row sample of the
-    same matrix, single thread; the sample is sized to stay near budget_s."""
-    import numpy as np
-
+def cpu_baseline(w, raw, x, g, gate, up, nt: int, budget_s: float = 20.0) -> dict:
+    """The oracle chain (the workload's producer, q8, GEMV) on the host over a row
+    sample of the same matrix, single thread; the sample is sized to stay near
+    budget_s and only the GEMV is timed."""
     import oracle
     import q6ksynth
 
-    xn = oracle.rmsnorm(x, g, q6ksynth.RMS_EPS)
+    if w.producer == "rmsnorm":
+        xn = oracle.rmsnorm(x, g, q6ksynth.RMS_EPS)
+    elif w.producer == "swiglu":
+        xn = oracle.swiglu(gate, up)
+    else:
+        xn = x
     qs, d = oracle.quant_q8(xn)
     probe = 2048
     t0 = time.perf_counter()
@@ -104,7 +110,7 @@ def cpu_baseline(w, raw, x, g, nt: int, budget_s: float = 20.0) -> dict:
     return {"value": round(content / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"first {rows} of {w.N} rows of the {w.N}x{w.K} matrix, nt={nt}, "
                       f"scalar C oracle GEMV (fp64), single thread, median of 3 runs "
-                      f"({t:.2f} s each); RMSNorm and q8 on the host excluded",
+                      f"({t:.2f} s each); the host producer and q8 not timed",
             "us_per_gemv_equiv": round(t / rows * w.N * 1e6, 1)}
 
 
@@ -153,6 +159,9 @@ def main() -> int:
     g = q6ksynth.gamma(K, q6ksynth.gamma_seed(w))
     x_d = torch.from_numpy(x).to(dev)
     g_d = torch.from_numpy(g).to(dev)
+    gate, up = q6ksynth.swiglu_pairs(w, nt)
+    gate_d = torch.from_numpy(gate).to(dev)
+    up_d = torch.from_numpy(up).to(dev)
     y_norm = torch.empty((nt, K), dtype=torch.float32, device=dev)
     plane = torch.empty(q.q8_plane_bytes(K, nt), dtype=torch.uint8, device=dev)
     y = torch.empty((nt, N), dtype=torch.float32, device=dev)
@@ -161,6 +170,8 @@ def main() -> int:
     def produce():
         if w.producer == "rmsnorm":
             q.rmsnorm_quant_q8(x_d, g_d, q6ksynth.RMS_EPS, y_norm, plane, K, nt, stream)
+        elif w.producer == "swiglu":
+            q.swiglu_quant_q8(gate_d, up_d, y_norm, plane, K, nt, stream)
         else:
             q.quant_q8(x_d, plane, K, nt, stream)
 
@@ -226,8 +237,7 @@ def main() -> int:
         "dtype": "int8",
         "data": "synthetic",
         "config": {"workload": f"{w.name} q6_K GEMV N={N} K={K} nt={nt}: "
-                               f"{'fused RMSNorm->q8' if w.producer == 'rmsnorm' else 'q8'} "
-                               f"producer + dpl q6_K x q8 MMVQ",
+                               f"{PRODUCER_NAMES[w.producer]} producer + dpl q6_K x q8 MMVQ",
                    "N": N, "K": K, "nt": nt, "content_bytes": content,
                    "dpl_bytes": dpl_bytes, "weight_copies": copies},
         "us_per_gemv": round(kern_us, 2),
@@ -244,7 +254,7 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on the host")
-        out["cpu_baseline"] = cpu_baseline(w, raw, x, g, nt)
+        out["cpu_baseline"] = cpu_baseline(w, raw, x, g, gate, up, nt)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -115,6 +115,15 @@ int quant_q8(const float *x, void *q8, int64_t K, int nt, void *stream);
 int rmsnorm_quant_q8(const float *x, const float *gamma, float eps, float *y, void *q8,
                      int64_t K, int nt, void *stream);
 
+/* Fused SwiGLU producer ([D3-5] §3.2, the fused swiglu producer): y = (g / (1 + e^-g))
+ * * u in f32 (IEEE division, the device library's expf), then the q8 body of quant_q8
+ * applied to y. g, u: float32 [nt][K] (e.g. the gate and up halves of one buffer);
+ * y: float32 [nt][K] (written; y may be exactly g or exactly u, i.e. in place, but
+ * may not otherwise overlap them); q8: as for quant_q8, overlapping none of g, u, y.
+ * All device, 16-B aligned, finite inputs; K a multiple of 32. */
+int swiglu_quant_q8(const float *g, const float *u, float *y, void *q8, int64_t K, int nt,
+                    void *stream);
+
 /* The MMVQ: y[t][r] = sum over super-blocks b and sub-blocks j of
  * f16(d_rb) * sc_rbj * f16(d8_t,8b+j/2) * D_trbj, with D the exact int32 dot of the
  * 16 codes (q - 32) and the 16 int8 activations of sub-block j ([D4-2] §3.2

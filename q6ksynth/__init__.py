@@ -31,6 +31,7 @@ class Workload:
     nt: tuple              # token columns exercised
     act: str               # "normal" | "outlier" | "swiglu"
     producer: str          # "quant" (standalone q8) | "rmsnorm" (fused RMSNorm -> q8)
+                           # | "swiglu" (fused SwiGLU -> q8 from gate/up rows)
 
     @property
     def nbe(self) -> int:
@@ -44,8 +45,8 @@ class Workload:
 WORKLOADS = {
     "tiny": Workload(1, "tiny", 64, 1024, (1,), "normal", "quant"),
     "attn_v": Workload(2, "attn_v", 1024, 5120, (1,), "outlier", "rmsnorm"),
-    "ffn_down": Workload(3, "ffn_down", 5120, 13824, (1,), "swiglu", "quant"),
-    "tall_k": Workload(4, "tall_k", 3584, 18944, (1,), "swiglu", "quant"),
+    "ffn_down": Workload(3, "ffn_down", 5120, 13824, (1,), "swiglu", "swiglu"),
+    "tall_k": Workload(4, "tall_k", 3584, 18944, (1,), "swiglu", "swiglu"),
     "lm_head": Workload(5, "lm_head", 152064, 5120, (1, 4), "outlier", "rmsnorm"),
 }
 
@@ -102,11 +103,29 @@ def activation(kind: str, K: int, seed: int) -> np.ndarray:
         x[idx] *= np.float32(50.0)
         return x
     if kind == "swiglu":
-        g = rng.standard_normal(K, dtype=np.float32)
-        u = rng.standard_normal(K, dtype=np.float32)
+        # the host-side f32 SwiGLU of the gate/up pair drawn by swiglu_pair(): the
+        # input of the standalone quantizer in the ffn_down-like workloads
+        g, u = _gate_up(rng, K)
         one = np.float32(1.0)
         return ((g / (one + np.exp(-g))) * u).astype(np.float32)
     raise ValueError(kind)
+
+
+def _gate_up(rng: np.random.Generator, K: int):
+    g = rng.standard_normal(K, dtype=np.float32)
+    u = rng.standard_normal(K, dtype=np.float32)
+    return g, u
+
+
+def swiglu_pair(K: int, seed: int):
+    """The gate and up rows (float32, N(0,1) each) of one SwiGLU activation."""
+    return _gate_up(np.random.default_rng(seed), K)
+
+
+def swiglu_pairs(w: Workload, nt: int):
+    """(g, u) float32 [nt, K] each; column c from its own seed."""
+    gu = [swiglu_pair(w.K, act_seed(w, c)) for c in range(nt)]
+    return np.stack([a for a, _ in gu]), np.stack([b for _, b in gu])
 
 
 def activations(w: Workload, nt: int) -> np.ndarray:

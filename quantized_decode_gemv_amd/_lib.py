@@ -32,6 +32,7 @@ _SIGS = {
     "repack_q6k_dpl": (_INT, [_P, _P, _I64, _I64, _P]),
     "quant_q8": (_INT, [_P, _P, _I64, _INT, _P]),
     "rmsnorm_quant_q8": (_INT, [_P, _P, ctypes.c_float, _P, _P, _I64, _INT, _P]),
+    "swiglu_quant_q8": (_INT, [_P, _P, _P, _P, _I64, _INT, _P]),
     "mmvq_q6k_q8": (_INT, [_P, _P, _P, _I64, _I64, _INT, _P]),
     "mmvq_q6k_q8_subdots": (_INT, [_P, _P, _P, _I64, _I64, _INT, _P]),
     "q6k_mmvq_plan": (_INT, [_I64, _I64, _INT, _INT, _P]),
@@ -162,6 +163,14 @@ def rmsnorm_quant_q8(x, gamma, eps: float, y, q8, K: int, nt: int, stream=None) 
     _need("q8", q8, q8_plane_bytes(K, nt))
     _call("rmsnorm_quant_q8", _addr(x), _addr(gamma), float(eps), _addr(y), _addr(q8), K, nt,
           _stream(stream))
+
+
+def swiglu_quant_q8(g, u, y, q8, K: int, nt: int, stream=None) -> None:
+    _need("g", g, 4 * K * max(nt, 0))
+    _need("u", u, 4 * K * max(nt, 0))
+    _need("y", y, 4 * K * max(nt, 0))
+    _need("q8", q8, q8_plane_bytes(K, nt))
+    _call("swiglu_quant_q8", _addr(g), _addr(u), _addr(y), _addr(q8), K, nt, _stream(stream))
 
 
 def mmvq_q6k_q8(w_dpl, q8, y, N: int, K: int, nt: int, stream=None) -> None:

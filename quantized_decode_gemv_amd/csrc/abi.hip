@@ -174,6 +174,23 @@ int rmsnorm_quant_q8(const float *x, const float *gamma, float eps, float *y, vo
         q6k::launch_rmsnorm_quant(x, gamma, eps, y, (uint8_t *)q8, K, nt, (hipStream_t)stream));
 }
 
+int swiglu_quant_q8(const float *g, const float *u, float *y, void *q8, int64_t K, int nt,
+                    void *stream)
+{
+    if (!act_shape_ok(K, nt))
+        return Q6K_E_SHAPE;
+    if (!g || !u || !y || !q8)
+        return Q6K_E_NULL;
+    if (!aligned16(g) || !aligned16(u) || !aligned16(y) || !aligned16(q8))
+        return Q6K_E_ALIGN;
+    const size_t nx = (size_t)nt * K * 4u, nq = q8_plane_bytes(K, nt);
+    // y may be g or u exactly (in place); any other overlap is refused
+    if ((y != g && overlap(y, nx, g, nx)) || (y != u && overlap(y, nx, u, nx)) ||
+        overlap(q8, nq, g, nx) || overlap(q8, nq, u, nx) || overlap(q8, nq, y, nx))
+        return Q6K_E_ALIAS;
+    return from_hip(q6k::launch_swiglu_quant(g, u, y, (uint8_t *)q8, K, nt, (hipStream_t)stream));
+}
+
 int mmvq_q6k_q8(const void *w_dpl, const void *q8, float *y, int64_t N, int64_t K, int nt,
                 void *stream)
 {

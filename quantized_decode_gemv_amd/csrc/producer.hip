@@ -1,5 +1,5 @@
-// producer.hip -- q8 activation producers for gfx950: the standalone quantizer and
-// the fused RMSNorm -> q8 producer.
+// producer.hip -- q8 activation producers for gfx950: the standalone quantizer, the
+// fused RMSNorm -> q8 producer and the fused SwiGLU -> q8 producer.
 //
 // The q8 body follows the per-32-block quantizer of D3-5 §3.2: amax = max|x|,
 // d = amax/127 (f32 division), di = d != 0 ? 1/d : 0 (f32 division),
@@ -68,6 +68,32 @@ __global__ __launch_bounds__(QWG) void quant_q8_kernel(const float4 *__restrict_
     const float4 v = live ? x[f] : make_float4(0.f, 0.f, 0.f, 0.f);
     const Q8Out o = quant_group8(v);
     if (live) {
+        qs[f] = o.packed;
+        if ((f & 7u) == 0)
+            d8[f >> 3] = o.d16;
+    }
+}
+
+// SwiGLU then q8 (D3-5 §3.2, the fused swiglu producer): y = (g / (1 + e^-g)) * u
+// in f32 -- IEEE division, the library expf -- stored and quantized from registers.
+// Each lane reads its g and u before it writes y, so y may be g or u itself.
+__global__ __launch_bounds__(QWG) void swiglu_quant_kernel(const float4 *g, const float4 *u,
+                                                           float4 *y, uint32_t *__restrict__ qs,
+                                                           uint16_t *__restrict__ d8, uint32_t nf4)
+{
+    const uint32_t f = blockIdx.x * QWG + threadIdx.x;
+    const bool live = f < nf4;
+    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 gv = live ? g[f] : zero;
+    const float4 uv = live ? u[f] : zero;
+    float4 yv;
+    yv.x = (gv.x / (1.0f + expf(-gv.x))) * uv.x;
+    yv.y = (gv.y / (1.0f + expf(-gv.y))) * uv.y;
+    yv.z = (gv.z / (1.0f + expf(-gv.z))) * uv.z;
+    yv.w = (gv.w / (1.0f + expf(-gv.w))) * uv.w;
+    const Q8Out o = quant_group8(yv);
+    if (live) {
+        y[f] = yv;
         qs[f] = o.packed;
         if ((f & 7u) == 0)
             d8[f >> 3] = o.d16;
@@ -201,6 +227,20 @@ hipError_t launch_quant(const float *x, uint8_t *q8, int64_t K, int nt, hipStrea
     const uint32_t grid = (nf4 + QWG - 1) / QWG;
     void *args[] = {(void *)&x4, (void *)&qs, (void *)&d8, (void *)&nf4};
     return hipLaunchKernel((const void *)quant_q8_kernel, dim3(grid), dim3(QWG), args, 0, s);
+}
+
+hipError_t launch_swiglu_quant(const float *g, const float *u, float *y, uint8_t *q8, int64_t K,
+                               int nt, hipStream_t s)
+{
+    const float4 *g4 = reinterpret_cast<const float4 *>(g);
+    const float4 *u4 = reinterpret_cast<const float4 *>(u);
+    float4 *y4 = reinterpret_cast<float4 *>(y);
+    uint32_t *qs = reinterpret_cast<uint32_t *>(q8);
+    uint16_t *d8 = reinterpret_cast<uint16_t *>(q8 + (size_t)nt * K);
+    uint32_t nf4 = (uint32_t)((int64_t)nt * K / 4);
+    const uint32_t grid = (nf4 + QWG - 1) / QWG;
+    void *args[] = {(void *)&g4, (void *)&u4, (void *)&y4, (void *)&qs, (void *)&d8, (void *)&nf4};
+    return hipLaunchKernel((const void *)swiglu_quant_kernel, dim3(grid), dim3(QWG), args, 0, s);
 }
 
 hipError_t launch_rmsnorm_quant(const float *x, const float *gamma, float eps, float *y,

@@ -28,6 +28,8 @@ hipError_t launch_subdots(const uint8_t *w, const uint8_t *q8, int32_t *dots, in
 hipError_t launch_quant(const float *x, uint8_t *q8, int64_t K, int nt, hipStream_t s);
 hipError_t launch_rmsnorm_quant(const float *x, const float *gamma, float eps, float *y,
                                 uint8_t *q8, int64_t K, int nt, hipStream_t s);
+hipError_t launch_swiglu_quant(const float *g, const float *u, float *y, uint8_t *q8, int64_t K,
+                               int nt, hipStream_t s);
 hipError_t launch_repack(const uint8_t *raw, uint8_t *dpl, int64_t N, int64_t K, hipStream_t s);
 void repack_host(const uint8_t *raw, uint8_t *dpl, int64_t N, int64_t K);
 void unpack_host(const uint8_t *dpl, uint8_t *raw, int64_t N, int64_t K);

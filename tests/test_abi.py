@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = set(declared_functions())
-    for n in ["repack_q6k_dpl", "rmsnorm_quant_q8", "mmvq_q6k_q8", "quant_q8",
+    for n in ["repack_q6k_dpl", "rmsnorm_quant_q8", "mmvq_q6k_q8", "quant_q8", "swiglu_quant_q8",
               "repack_q6k_dpl_host", "unpack_q6k_dpl_host", "mmvq_q6k_q8_subdots",
               "q6k_strerror", "q6k_dpl_row_stride", "q8_plane_bytes"]:
         assert n in names
@@ -130,6 +130,18 @@ def test_producers_reject_bad_arguments():
     assert _code(q.rmsnorm_quant_q8, A, B, 1e-6, A, D, 64, 1, 0) == E_ALIAS
     assert _code(q.rmsnorm_quant_q8, A, B, 1e-6, C, C + 16, 64, 1, 0) == E_ALIAS
     assert _code(q.rmsnorm_quant_q8, A, B, 1e-6, C, B, 64, 1, 0) == E_ALIAS
+
+
+def test_swiglu_producer_rejects_bad_arguments():
+    assert _code(q.swiglu_quant_q8, A, B, C, D, 40, 1, 0) == E_SHAPE
+    assert _code(q.swiglu_quant_q8, A, B, C, D, 64, 0, 0) == E_SHAPE
+    assert _code(q.swiglu_quant_q8, A, None, C, D, 64, 1, 0) == E_NULL
+    assert _code(q.swiglu_quant_q8, A, B + 4, C, D, 64, 1, 0) == E_ALIGN
+    # y overlapping g or u partially (not exactly in place), q8 overlapping anything
+    assert _code(q.swiglu_quant_q8, A, B, A + 16, D, 64, 1, 0) == E_ALIAS
+    assert _code(q.swiglu_quant_q8, A, B, B - 16, D, 64, 1, 0) == E_ALIAS
+    assert _code(q.swiglu_quant_q8, A, B, C, A + 32, 64, 1, 0) == E_ALIAS
+    assert _code(q.swiglu_quant_q8, A, B, C, C, 64, 1, 0) == E_ALIAS
 
 
 def test_device_repack_rejects_bad_arguments():

@@ -27,6 +27,12 @@ def _chain(w: q6ksynth.Workload, nt: int):
         q.rmsnorm_quant_q8(dev_f32(x), dev_f32(g), q6ksynth.RMS_EPS, yd, plane, w.K, nt)
         x_or = oracle.rmsnorm(x, g, q6ksynth.RMS_EPS)
         x_gpu = yd.cpu().numpy()
+    elif w.producer == "swiglu":
+        gate, up = q6ksynth.swiglu_pairs(w, nt)
+        yd = torch.empty((nt, w.K), dtype=torch.float32, device=DEV)
+        q.swiglu_quant_q8(dev_f32(gate), dev_f32(up), yd, plane, w.K, nt)
+        x_or = oracle.swiglu(gate, up)
+        x_gpu = yd.cpu().numpy()
     else:
         q.quant_q8(dev_f32(x), plane, w.K, nt)
         x_or = x_gpu = x

@@ -110,3 +110,43 @@ def test_rmsnorm_zero_row_is_zero():
     assert not y.cpu().numpy().any()
     qs, d = split_plane(plane, K, 1)
     assert not qs.any() and not d.any()
+
+
+# --- fused SwiGLU -> q8 -------------------------------------------------------------
+
+def _swiglu_tol(y_or):
+    # f32 body: expf (about 1 ulp), 1 + e, the division and the product each round:
+    # within 4 ulp of the exactly rounded value
+    return 4 * np.spacing(np.abs(y_or).astype(np.float32)).astype(np.float64)
+
+
+@pytest.mark.parametrize("K", [32, 256, 5120, 13824, 18944])
+@pytest.mark.parametrize("nt", [1, 4, 5])
+def test_swiglu_quant_q8(K, nt):
+    g, u = (np.stack(a) for a in zip(*[q6ksynth.swiglu_pair(K, 800 + c) for c in range(nt)]))
+    g[0, :8] = [0.0, 40.0, -40.0, 88.0, -88.0, 1e-30, -3.0, 3.0]   # saturation and zeros
+    y = torch.empty((nt, K), dtype=torch.float32, device=DEV)
+    plane = q8_plane(K, nt)
+    q.swiglu_quant_q8(dev_f32(g), dev_f32(u), y, plane, K, nt)
+    y_gpu = y.cpu().numpy()
+    y_or = oracle.swiglu(g, u)
+    assert np.all(np.abs(y_gpu.astype(np.float64) - y_or) <= _swiglu_tol(y_or))
+    qs, d = split_plane(plane, K, nt)
+    qs_or, d_or = oracle.quant_q8(y_or)
+    rep = check_plane_vs_oracle_chain(y_gpu, y_or, qs, d, qs_or, d_or, f"swiglu K={K} nt={nt}")
+    say(f"swiglu K={K} nt={nt}: y bit-equal fraction {np.mean(y_gpu == y_or):.4f}; {rep}")
+
+
+@pytest.mark.parametrize("which", ["g", "u"])
+def test_swiglu_in_place(which):
+    K, nt = 5120, 2
+    g, u = (np.stack(a) for a in zip(*[q6ksynth.swiglu_pair(K, 810 + c) for c in range(nt)]))
+    gd, ud = dev_f32(g), dev_f32(u)
+    ref = torch.empty((nt, K), dtype=torch.float32, device=DEV)
+    p_ref = q8_plane(K, nt)
+    q.swiglu_quant_q8(gd, ud, ref, p_ref, K, nt)
+    p_in = q8_plane(K, nt)
+    out = gd if which == "g" else ud
+    q.swiglu_quant_q8(gd, ud, out, p_in, K, nt)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref) and torch.equal(p_in, p_ref)
