@@ -123,6 +123,8 @@ def main() -> int:
     ap.add_argument("--workload", default="lm_head")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
+    ap.add_argument("--graph", type=int, default=0, metavar="G",
+                    help="run the timed steps as replays of a HIP graph holding G steps")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -183,14 +185,43 @@ def main() -> int:
         gemv(i)
     torch.cuda.synchronize()
 
-    # The step loop: producer then GEMV, weights rotating, nothing else queued.
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        produce()
-        gemv(i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # The step loop: producer then GEMV, weights rotating, nothing else queued. With
+    # --graph G the same launches are captured G steps at a time into one HIP graph
+    # (weights still rotating inside it) and the graph is replayed.
+    if args.graph > 0:
+        G = args.graph
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                for i in range(G):
+                    if w.producer == "rmsnorm":
+                        q.rmsnorm_quant_q8(x_d, g_d, q6ksynth.RMS_EPS, y_norm, plane, K, nt, side)
+                    elif w.producer == "swiglu":
+                        q.swiglu_quant_q8(gate_d, up_d, y_norm, plane, K, nt, side)
+                    else:
+                        q.quant_q8(x_d, plane, K, nt, side)
+                    q.mmvq_q6k_q8(Ws[i % copies], plane, y, N, K, nt, side)
+        torch.cuda.synchronize()
+        for _ in range(max(1, args.warmup // G)):
+            graph.replay()
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // G)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms_per_step = (t1 - t0) * 1e3 / (reps * G)
+    else:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            produce()
+            gemv(i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms_per_step = (t1 - t0) * 1e3 / args.steps
 
     # The GEMV alone: the same launches back to back on the same stream between two
     # HIP events recorded on that stream; mean duration per launch.
@@ -248,6 +279,7 @@ def main() -> int:
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
         "mmvq_plan": plan,
+        "step_launch": f"hip graph of {args.graph} steps" if args.graph > 0 else "eager",
         "kernel_sha": kernel_hash(),
         "baseline_note": "vs_baseline divides by the pages' 250.0 GB/s dpl lm_head content "
                          "rate, measured on an NVIDIA GB10: context, not a target",
