@@ -1,18 +1,20 @@
 #!/usr/bin/env python3
 """Benchmark of the q6_K x q8 decode GEMV path on one MI355X.
 
-A step is one pass of the hot path over one batch: the fused RMSNorm -> q8
-producer on the activation row(s), then the q6_K (dpl) x q8 GEMV over the
-152064 x 5120 lm_head matrix (638.67 MB of q6_K content). Inputs are resident in
-HBM before timing starts. The weights rotate over enough device copies (>= 1 GiB
-in total) that the 256 MB last-level cache cannot serve them from one step to the
-next.
+A step is one pass of the hot path over one batch: RMSNorm -> q8 on the
+activation row(s) and the q6_K (dpl) x q8 GEMV over the 152064 x 5120 lm_head
+matrix (638.67 MB of q6_K content). By default the step is the library's fused
+RMSNorm -> q8 -> GEMV call (one kernel); --path split runs the producer kernel then
+the GEMV kernel. Inputs are resident in HBM before timing starts. The weights
+rotate over enough device copies (>= 1 GiB in total) that the 256 MB last-level
+cache cannot serve them from one step to the next.
 
-Prints one JSON line: content GB/s of the whole step (`value`), the GEMV kernel's
-own rate against the 8 TB/s HBM peak (`roofline`, timed with HIP events on the
-stream the kernels run on), and the oracle timed on host cores (`cpu_baseline`).
+Prints one JSON line: content GB/s of the whole step (`value`), the dominant
+kernel's own rate against the 8 TB/s HBM peak (`roofline`, timed with HIP events on
+the stream the kernels run on), and the oracle timed on host cores (`cpu_baseline`).
 
-    python bench.py [--gpus 1] [--steps 300] [--warmup 100] [--nt 1] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 300] [--warmup 100] [--nt 1] [--path fused|split]
+                    [--no-cpu-baseline]
     python bench.py --copy-calib    # plain device copy of known size, for counter scaling
 """
 from __future__ import annotations
@@ -37,7 +39,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mmvq_lm_head_traffic.txt")
 PRODUCER_NAMES = {"rmsnorm": "fused RMSNorm->q8", "swiglu": "fused SwiGLU->q8",
                   "quant": "q8"}
 KERNEL_SOURCES = [os.path.join(ROOT, "quantized_decode_gemv_amd", "csrc", f)
-                  for f in ("mmvq.hip", "q6k_unit.h")]
+                  for f in ("mmvq.hip", "q6k_unit.h", "q6k_norm.h")]
 
 
 def log(*a):
@@ -52,9 +54,10 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(nt: int):
-    """HBM bytes per GEMV launch from the committed counter summary, or None when
-    the summary is absent or was taken on a different kernel source."""
+def recorded_traffic(key: str):
+    """HBM bytes per launch of the dominant kernel (key: e.g. fused_nt1, gemv_nt4)
+    from the committed counter summary, or None when the summary is absent or was
+    taken on a different kernel source."""
     try:
         kv = {}
         with open(TRAFFIC_FILE) as f:
@@ -64,7 +67,7 @@ def recorded_traffic(nt: int):
                     kv[parts[0]] = parts[1]
         if kv.get("kernel_sha") != kernel_hash():
             return None
-        return float(kv[f"bytes_per_launch_nt{nt}"])
+        return float(kv[f"bytes_per_launch_{key}"])
     except (OSError, KeyError, ValueError):
         return None
 
@@ -123,6 +126,9 @@ def main() -> int:
     ap.add_argument("--workload", default="lm_head")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
+    ap.add_argument("--path", choices=["fused", "split"], default="fused",
+                    help="fused: one RMSNorm -> q8 -> GEMV call per step (RMSNorm workloads "
+                         "only); split: the producer kernel, then the GEMV kernel")
     ap.add_argument("--graph", type=int, default=0, metavar="G",
                     help="run the timed steps as replays of a HIP graph holding G steps")
     args = ap.parse_args()
@@ -168,26 +174,57 @@ def main() -> int:
     plane = torch.empty(q.q8_plane_bytes(K, nt), dtype=torch.uint8, device=dev)
     y = torch.empty((nt, N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    fused = args.path == "fused" and w.producer == "rmsnorm"
 
-    def produce():
+    def produce(st):
         if w.producer == "rmsnorm":
-            q.rmsnorm_quant_q8(x_d, g_d, q6ksynth.RMS_EPS, y_norm, plane, K, nt, stream)
+            q.rmsnorm_quant_q8(x_d, g_d, q6ksynth.RMS_EPS, y_norm, plane, K, nt, st)
         elif w.producer == "swiglu":
-            q.swiglu_quant_q8(gate_d, up_d, y_norm, plane, K, nt, stream)
+            q.swiglu_quant_q8(gate_d, up_d, y_norm, plane, K, nt, st)
         else:
-            q.quant_q8(x_d, plane, K, nt, stream)
+            q.quant_q8(x_d, plane, K, nt, st)
 
-    def gemv(i):
-        q.mmvq_q6k_q8(Ws[i % copies], plane, y, N, K, nt, stream)
+    def gemv(i, st):
+        q.mmvq_q6k_q8(Ws[i % copies], plane, y, N, K, nt, st)
+
+    def fused_call(i, st):
+        q.mmvq_q6k_rmsnorm_q8(Ws[i % copies], x_d, g_d, q6ksynth.RMS_EPS, None, plane, y,
+                              N, K, nt, st)
+
+    def split_step(i, st):
+        produce(st)
+        gemv(i, st)
+
+    step = fused_call if fused else split_step
+
+    def time_steps(fn, n):
+        t0 = time.perf_counter()
+        for i in range(n):
+            fn(i, stream)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n
+
+    def time_back_to_back(fn, n):
+        """Launches back to back on the stream between two HIP events recorded on
+        that stream; mean duration per launch."""
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(i, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
 
     for i in range(args.warmup):
-        produce()
-        gemv(i)
+        step(i, stream)
+        if fused:
+            split_step(i, stream)
     torch.cuda.synchronize()
 
-    # The step loop: producer then GEMV, weights rotating, nothing else queued. With
-    # --graph G the same launches are captured G steps at a time into one HIP graph
-    # (weights still rotating inside it) and the graph is replayed.
+    # The step loop: weights rotating, nothing else queued. With --graph G the same
+    # launches are captured G steps at a time into one HIP graph (weights still
+    # rotating inside it) and the graph is replayed.
     if args.graph > 0:
         G = args.graph
         graph = torch.cuda.CUDAGraph()
@@ -196,13 +233,7 @@ def main() -> int:
         with torch.cuda.stream(side):
             with torch.cuda.graph(graph, stream=side):
                 for i in range(G):
-                    if w.producer == "rmsnorm":
-                        q.rmsnorm_quant_q8(x_d, g_d, q6ksynth.RMS_EPS, y_norm, plane, K, nt, side)
-                    elif w.producer == "swiglu":
-                        q.swiglu_quant_q8(gate_d, up_d, y_norm, plane, K, nt, side)
-                    else:
-                        q.quant_q8(x_d, plane, K, nt, side)
-                    q.mmvq_q6k_q8(Ws[i % copies], plane, y, N, K, nt, side)
+                    step(i, side)
         torch.cuda.synchronize()
         for _ in range(max(1, args.warmup // G)):
             graph.replay()
@@ -212,36 +243,23 @@ def main() -> int:
         for _ in range(reps):
             graph.replay()
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        ms_per_step = (t1 - t0) * 1e3 / (reps * G)
+        ms_per_step = (time.perf_counter() - t0) * 1e3 / (reps * G)
     else:
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            produce()
-            gemv(i)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        ms_per_step = (t1 - t0) * 1e3 / args.steps
+        ms_per_step = time_steps(step, args.steps)
+    ms_per_step_split = time_steps(split_step, args.steps) if fused else None
 
-    # The GEMV alone: the same launches back to back on the same stream between two
-    # HIP events recorded on that stream; mean duration per launch.
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        gemv(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    kern_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    # The dominant kernel alone: the fused kernel (fused path) or the GEMV kernel.
+    kern_us = time_back_to_back(fused_call if fused else gemv, args.steps)
+    gemv_us = time_back_to_back(gemv, args.steps) if fused else kern_us
 
     # Diagnostic: events around every GEMV inside producer+GEMV steps (these also
     # count each launch's dispatch latency).
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(min(args.steps, 100))]
     for i, (a, b) in enumerate(evs):
-        produce()
+        produce(stream)
         a.record(stream)
-        gemv(i)
+        gemv(i, stream)
         b.record(stream)
     torch.cuda.synchronize()
     inline = [a.elapsed_time(b) * 1e3 for a, b in evs]
@@ -251,7 +269,7 @@ def main() -> int:
     content = w.content_bytes
     value = content / (ms_per_step * 1e-3) / 1e9
     achieved = content / (kern_us * 1e-6) / 1e9
-    traffic = recorded_traffic(nt)
+    traffic = recorded_traffic(f"{'fused' if fused else 'gemv'}_nt{nt}")
     plan = q.mmvq_plan(N, K, nt, torch.cuda.get_device_properties(0).multi_processor_count)
 
     out = {
@@ -268,10 +286,14 @@ def main() -> int:
         "dtype": "int8",
         "data": "synthetic",
         "config": {"workload": f"{w.name} q6_K GEMV N={N} K={K} nt={nt}: "
-                               f"{PRODUCER_NAMES[w.producer]} producer + dpl q6_K x q8 MMVQ",
+                               + (f"RMSNorm->q8->dpl q6_K x q8 MMVQ in one kernel" if fused else
+                                  f"{PRODUCER_NAMES[w.producer]} producer + dpl q6_K x q8 MMVQ"),
                    "N": N, "K": K, "nt": nt, "content_bytes": content,
                    "dpl_bytes": dpl_bytes, "weight_copies": copies},
-        "us_per_gemv": round(kern_us, 2),
+        "dominant_kernel": "mmvq_rmsnorm_rows (fused)" if fused else "mmvq_rows",
+        "us_per_dominant_kernel": round(kern_us, 2),
+        "us_per_gemv": round(gemv_us, 2),
+        "ms_per_step_split": round(ms_per_step_split, 5) if fused else None,
         "us_per_gemv_inline_events": {"mean": round(kern_inline_us, 2),
                                       "median": round(kern_inline_med_us, 2)},
         "pct_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),

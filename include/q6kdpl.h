@@ -136,6 +136,26 @@ int swiglu_quant_q8(const float *g, const float *u, float *y, void *q8, int64_t 
 int mmvq_q6k_q8(const void *w_dpl, const void *q8, float *y, int64_t N, int64_t K, int nt,
                 void *stream);
 
+/* RMSNorm -> q8 -> MMVQ in one call: the outputs of
+ *   rmsnorm_quant_q8(x, gamma, eps, xn, q8, K, nt) then mmvq_q6k_q8(w_dpl, q8, y, N, K, nt),
+ * bit for bit ([D3-5] §3.2, the fused rms producer and the per-32-block body; [D4-2]
+ * §3.2 Excerpt C and [D4-4] §3.2 Excerpt B for the MMVQ). Where
+ * q6k_rmsnorm_mmvq_fused(N, K, nt) is 1 (one token, K <= 12288) this is a single
+ * kernel: each workgroup normalizes and quantizes the activations itself and the
+ * weight stream starts before the norm ends; otherwise the two kernels are queued.
+ * w_dpl: q6k_dpl_bytes(N, K) device bytes; x: float32 [nt][K]; gamma: float32 [K];
+ * xn: float32 [nt][K] written with the normalized rows, or NULL to skip them; q8:
+ * q8_plane_bytes(K, nt) device bytes, written (the q8 plane of xn, reusable by
+ * mmvq_q6k_q8 for other weights); y: float32 [nt][N], written. All device, 16-B
+ * aligned; no output may overlap an input or another output. K a multiple of 256. */
+int mmvq_q6k_rmsnorm_q8(const void *w_dpl, const float *x, const float *gamma, float eps,
+                        float *xn, void *q8, float *y, int64_t N, int64_t K, int nt,
+                        void *stream);
+
+/* Diagnostics: 1 when mmvq_q6k_rmsnorm_q8 runs (N, K, nt) as one fused kernel, 0
+ * when it queues the producer and the MMVQ, Q6K_E_SHAPE on a bad shape. Host only. */
+int q6k_rmsnorm_mmvq_fused(int64_t N, int64_t K, int nt);
+
 /* Test entry: the exact sub-block dots D of mmvq_q6k_q8, dots[(t*N + r)*(K/16) + j]
  * (int32, device, 16-B aligned, nt*N*(K/16) entries). Same inputs as mmvq_q6k_q8. */
 int mmvq_q6k_q8_subdots(const void *w_dpl, const void *q8, int32_t *dots, int64_t N, int64_t K,

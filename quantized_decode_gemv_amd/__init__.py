@@ -10,7 +10,7 @@ from __future__ import annotations
 
 from ._lib import (  # noqa: F401
     LIB_PATH, Q6K_MAX_K, Q6K_MAX_N, Q6K_MAX_NT, Q6kError, lib, load, mmvq_plan,
-    mmvq_q6k_q8, mmvq_q6k_q8_subdots, q6k_dpl_bytes, q6k_dpl_row_stride, q6k_raw_bytes,
+    mmvq_q6k_q8, mmvq_q6k_q8_subdots, mmvq_q6k_rmsnorm_q8, q6k_dpl_bytes, q6k_dpl_row_stride, q6k_raw_bytes,
     q6k_version, q8_plane_bytes, quant_q8, repack_q6k_dpl, repack_q6k_dpl_host,
-    rmsnorm_quant_q8, swiglu_quant_q8, unpack_q6k_dpl_host,
+    rmsnorm_mmvq_fused, rmsnorm_quant_q8, swiglu_quant_q8, unpack_q6k_dpl_host,
 )

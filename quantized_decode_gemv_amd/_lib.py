@@ -35,6 +35,9 @@ _SIGS = {
     "swiglu_quant_q8": (_INT, [_P, _P, _P, _P, _I64, _INT, _P]),
     "mmvq_q6k_q8": (_INT, [_P, _P, _P, _I64, _I64, _INT, _P]),
     "mmvq_q6k_q8_subdots": (_INT, [_P, _P, _P, _I64, _I64, _INT, _P]),
+    "mmvq_q6k_rmsnorm_q8": (_INT, [_P, _P, _P, ctypes.c_float, _P, _P, _P, _I64, _I64, _INT,
+                                   _P]),
+    "q6k_rmsnorm_mmvq_fused": (_INT, [_I64, _I64, _INT]),
     "q6k_mmvq_plan": (_INT, [_I64, _I64, _INT, _INT, _P]),
 }
 
@@ -178,6 +181,26 @@ def mmvq_q6k_q8(w_dpl, q8, y, N: int, K: int, nt: int, stream=None) -> None:
     _need("q8", q8, q8_plane_bytes(K, nt))
     _need("y", y, 4 * max(N, 0) * max(nt, 0))
     _call("mmvq_q6k_q8", _addr(w_dpl), _addr(q8), _addr(y), N, K, nt, _stream(stream))
+
+
+def mmvq_q6k_rmsnorm_q8(w_dpl, x, gamma, eps: float, xn, q8, y, N: int, K: int, nt: int,
+                        stream=None) -> None:
+    _need("w_dpl", w_dpl, q6k_dpl_bytes(N, K))
+    _need("x", x, 4 * K * max(nt, 0))
+    _need("gamma", gamma, 4 * K)
+    if xn is not None:
+        _need("xn", xn, 4 * K * max(nt, 0))
+    _need("q8", q8, q8_plane_bytes(K, nt))
+    _need("y", y, 4 * max(N, 0) * max(nt, 0))
+    _call("mmvq_q6k_rmsnorm_q8", _addr(w_dpl), _addr(x), _addr(gamma), float(eps), _addr(xn),
+          _addr(q8), _addr(y), N, K, nt, _stream(stream))
+
+
+def rmsnorm_mmvq_fused(N: int, K: int, nt: int) -> bool:
+    rc = lib().q6k_rmsnorm_mmvq_fused(N, K, nt)
+    if rc < 0:
+        raise Q6kError("q6k_rmsnorm_mmvq_fused", rc)
+    return bool(rc)
 
 
 def mmvq_q6k_q8_subdots(w_dpl, q8, dots, N: int, K: int, nt: int, stream=None) -> None:

@@ -19,6 +19,9 @@ HIPCC_FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
     # no packed-FP32 instruction forms (v_pk_*_f32) in any device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no implicit multiply-add contraction: every fused multiply-add is written out,
+    # so kernels that share arithmetic round identically
+    "-ffp-contract=off",
     "-Wall", "-Wno-unused-result",
 ]
 

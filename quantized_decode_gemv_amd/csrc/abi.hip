@@ -211,6 +211,47 @@ int mmvq_q6k_q8(const void *w_dpl, const void *q8, float *y, int64_t N, int64_t 
                                      cu, (hipStream_t)stream));
 }
 
+int mmvq_q6k_rmsnorm_q8(const void *w_dpl, const float *x, const float *gamma, float eps,
+                        float *xn, void *q8, float *y, int64_t N, int64_t K, int nt, void *stream)
+{
+    if (!weight_shape_ok(N, K) || !act_shape_ok(K, nt))
+        return Q6K_E_SHAPE;
+    if (!w_dpl || !x || !gamma || !q8 || !y)
+        return Q6K_E_NULL;
+    if (!aligned16(w_dpl) || !aligned16(x) || !aligned16(gamma) || !aligned16(q8) ||
+        !aligned16(y) || (xn && !aligned16(xn)))
+        return Q6K_E_ALIGN;
+    const size_t nw = q6k_dpl_bytes(N, K), nx = (size_t)nt * K * 4u, ng = (size_t)K * 4u;
+    const size_t nq = q8_plane_bytes(K, nt), ny = (size_t)nt * N * 4u;
+    // every output against every input and every other output
+    const void *in[3] = {w_dpl, x, gamma};
+    const size_t in_n[3] = {nw, nx, ng};
+    const void *out[3] = {q8, y, xn};
+    const size_t out_n[3] = {nq, ny, xn ? nx : 0};
+    for (int o = 0; o < 3; ++o) {
+        for (int i = 0; i < 3; ++i)
+            if (overlap(out[o], out_n[o], in[i], in_n[i]))
+                return Q6K_E_ALIAS;
+        for (int p = o + 1; p < 3; ++p)
+            if (overlap(out[o], out_n[o], out[p], out_n[p]))
+                return Q6K_E_ALIAS;
+    }
+    int cu = 0;
+    int rc = cu_count((hipStream_t)stream, &cu);
+    if (rc != Q6K_OK)
+        return rc;
+    return from_hip(q6k::launch_rmsnorm_mmvq((const uint8_t *)w_dpl, x, gamma, eps, xn,
+                                             (uint8_t *)q8, y, N, K, nt, cu,
+                                             (hipStream_t)stream));
+}
+
+int q6k_rmsnorm_mmvq_fused(int64_t N, int64_t K, int nt)
+{
+    if (!weight_shape_ok(N, K) || !act_shape_ok(K, nt))
+        return Q6K_E_SHAPE;
+    return q6k::rmsnorm_mmvq_fused(K, nt) ? 1 : 0;
+}
+
 int mmvq_q6k_q8_subdots(const void *w_dpl, const void *q8, int32_t *dots, int64_t N, int64_t K,
                         int nt, void *stream)
 {

@@ -36,6 +36,7 @@
 // a shape to a kernel covering fewer units silently drops work).
 
 #include "q6k_internal.h"
+#include "q6k_norm.h"
 #include "q6k_unit.h"
 
 namespace q6k {
@@ -88,6 +89,22 @@ __device__ __forceinline__ ChunkW load_chunk(__amdgpu_buffer_rsrc_t r, const Chu
     w.sc = make_uint2(c.x, c.y);
     w.d = d;
     return w;
+}
+
+// Descriptor of n float4s; loads past them return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t f4_desc(const float4 *p, uint32_t n)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void *)p, (short)0, (int)(16u * n), DESC_WORD3);
+}
+
+__device__ __forceinline__ float4 load_f4(__amdgpu_buffer_rsrc_t r, uint32_t f)
+{
+    const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(16u * f), 0, POLICY_DEFAULT);
+    // elements are copied into plain integers before their bit casts: a bit cast
+    // applied straight to a vector element reads element 0
+    const uint32_t a = v.x, b = v.y, c = v.z, d = v.w;
+    return make_float4(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b),
+                       __builtin_bit_cast(float, c), __builtin_bit_cast(float, d));
 }
 
 template <int CTRL>
@@ -165,9 +182,8 @@ struct LaneState {
 };
 
 template <int NT, int CPL, bool HOIST>
-__device__ __forceinline__ void lane_init(LaneState<NT, CPL, HOIST> &st, uint32_t lane,
-                                          uint32_t nbe, const int8_t *qs, const uint16_t *d8,
-                                          uint32_t K)
+__device__ __forceinline__ void lane_chunks(LaneState<NT, CPL, HOIST> &st, uint32_t lane,
+                                            uint32_t nbe)
 {
     const uint32_t C = 8u * nbe;
 #pragma unroll
@@ -176,12 +192,31 @@ __device__ __forceinline__ void lane_init(LaneState<NT, CPL, HOIST> &st, uint32_
         st.live[i] = Q < C;
         st.Q[i] = st.live[i] ? Q : C - 1u;
         st.off[i] = chunk_offsets(st.Q[i], nbe);
-        if constexpr (HOIST) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                st.act[i][t] = load_act(qs + (size_t)t * K, d8 + (size_t)t * (K / 32), st.Q[i]);
-        }
     }
+}
+
+// qs, d8: the activation rows (global memory or LDS), token t at qs + t * K and
+// d8 + t * (K / 32).
+template <int NT, int CPL>
+__device__ __forceinline__ void lane_acts(LaneState<NT, CPL, true> &st, const int8_t *qs,
+                                          const uint16_t *d8, uint32_t K)
+{
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            st.act[i][t] = load_act(qs + (size_t)t * K, d8 + (size_t)t * (K / 32), st.Q[i]);
+    }
+}
+
+template <int NT, int CPL, bool HOIST>
+__device__ __forceinline__ void lane_init(LaneState<NT, CPL, HOIST> &st, uint32_t lane,
+                                          uint32_t nbe, const int8_t *qs, const uint16_t *d8,
+                                          uint32_t K)
+{
+    lane_chunks(st, lane, nbe);
+    if constexpr (HOIST)
+        lane_acts(st, qs, d8, K);
 }
 
 template <int NT, int CPL, bool HOIST>
@@ -212,11 +247,11 @@ __device__ __forceinline__ void finish_row(const ChunkW (&src)[CPL],
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             if constexpr (HOIST) {
-                acc[t] += chunk_partial_d(src[i], st.act[i][t], st.Q[i], d);
+                acc[t] = chunk_accumulate(acc[t], src[i], st.act[i][t], st.Q[i], d);
             } else {
                 const ChunkAct a =
                     load_act(qs + (size_t)t * K, d8 + (size_t)t * (K / 32), st.Q[i]);
-                acc[t] += chunk_partial_d(src[i], a, st.Q[i], d);
+                acc[t] = chunk_accumulate(acc[t], src[i], a, st.Q[i], d);
             }
         }
     }
@@ -226,34 +261,44 @@ __device__ __forceinline__ void finish_row(const ChunkW (&src)[CPL],
         y[(size_t)t * ldy + row] = s;
 }
 
-// Rows with at most MAX_CPL chunks per lane; DEPTH rows in flight per wave.
-template <int NT, int CPL, int DEPTH, bool HOIST>
-__global__ __launch_bounds__(WG) void mmvq_rows(const uint8_t *__restrict__ w,
-                                                const int8_t *__restrict__ qs,
-                                                const uint16_t *__restrict__ d8,
-                                                float *__restrict__ y, uint32_t N, uint32_t nbe,
-                                                uint32_t stride, uint32_t K, uint32_t ldy)
+// Requests rows FROM .. TO - 1 of a wave's walk (row, row + nw, ...), the first
+// DEPTH of which go to A, B and Cb in that order.
+template <int NT, int CPL, int FROM, int TO, bool HOIST>
+__device__ __forceinline__ void prime_rows(ChunkW (&A)[CPL], ChunkW (&B)[CPL], ChunkW (&Cb)[CPL],
+                                           const uint8_t *w, uint32_t row, uint32_t nw,
+                                           uint32_t N, uint32_t stride,
+                                           const LaneState<NT, CPL, HOIST> &st)
 {
-    const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t wave = blockIdx.x * WAVES_PER_WG + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t nw = gridDim.x * WAVES_PER_WG;
-    LaneState<NT, CPL, HOIST> st;
-    lane_init(st, lane, nbe, qs, d8, K);
-    if (wave >= N)
-        return;
+    if constexpr (FROM <= 0 && TO > 0)
+        load_row(A, w, row, N, stride, st);
+    if constexpr (FROM <= 1 && TO > 1)
+        load_row(B, w, row + nw, N, stride, st);
+    if constexpr (FROM <= 2 && TO > 2)
+        load_row(Cb, w, row + 2u * nw, N, stride, st);
+}
+
+// A wave's walk over rows row, row + nw, ... < N with DEPTH rows in flight, the
+// first DEPTH - 1 of them already requested by prime_rows. Each step requests the
+// row DEPTH - 1 ahead, then reduces the oldest (the loads of a step always come
+// first in the loop body: with the reduction first, the compiler waits for every
+// load at the loop head).
+template <int NT, int CPL, int DEPTH, bool HOIST>
+__device__ __forceinline__ void stream_rows(ChunkW (&A)[CPL], ChunkW (&B)[CPL], ChunkW (&Cb)[CPL],
+                                            const uint8_t *w, uint32_t row, uint32_t nw,
+                                            uint32_t N, uint32_t stride,
+                                            const LaneState<NT, CPL, HOIST> &st, const int8_t *qs,
+                                            const uint16_t *d8, uint32_t K, float *y, uint32_t ldy,
+                                            uint32_t lane)
+{
     // look-ahead rows past the end get an empty descriptor (load_row), so every load
     // stays unconditional and their results are never reduced
 #define Q6K_FINISH(BUF, ROW) finish_row<NT, CPL, HOIST>(BUF, st, qs, d8, K, y, ldy, ROW, lane)
     if constexpr (DEPTH == 1) {
-        ChunkW A[CPL];
-        for (uint32_t row = wave; row < N; row += nw) {
+        for (; row < N; row += nw) {
             load_row(A, w, row, N, stride, st);
             Q6K_FINISH(A, row);
         }
     } else if constexpr (DEPTH == 2) {
-        ChunkW A[CPL], B[CPL];
-        uint32_t row = wave;
-        load_row(A, w, row, N, stride, st);
         for (;;) {
             const uint32_t r1 = row + nw;
             load_row(B, w, r1, N, stride, st);
@@ -270,10 +315,6 @@ __global__ __launch_bounds__(WG) void mmvq_rows(const uint8_t *__restrict__ w,
             row = r2;
         }
     } else {
-        ChunkW A[CPL], B[CPL], Cb[CPL];
-        uint32_t row = wave;
-        load_row(A, w, row, N, stride, st);
-        load_row(B, w, row + nw, N, stride, st);
         for (;;) {
             const uint32_t r1 = row + nw, r2 = r1 + nw, r3 = r2 + nw;
             load_row(Cb, w, r2, N, stride, st);
@@ -294,7 +335,162 @@ __global__ __launch_bounds__(WG) void mmvq_rows(const uint8_t *__restrict__ w,
             row = r3;
         }
     }
+}
+
+// The same walk with all DEPTH first rows already requested: one step of the
+// walk peeled off without its first request, then stream_rows from the next row.
+template <int NT, int CPL, int DEPTH, bool HOIST>
+__device__ __forceinline__ void stream_rows_primed(ChunkW (&A)[CPL], ChunkW (&B)[CPL],
+                                                   ChunkW (&Cb)[CPL], const uint8_t *w,
+                                                   uint32_t row, uint32_t nw, uint32_t N,
+                                                   uint32_t stride,
+                                                   const LaneState<NT, CPL, HOIST> &st,
+                                                   const int8_t *qs, const uint16_t *d8,
+                                                   uint32_t K, float *y, uint32_t ldy,
+                                                   uint32_t lane)
+{
+    const uint32_t r1 = row + nw, r2 = r1 + nw, r3 = r2 + nw;
+    Q6K_FINISH(A, row);
+    if (r1 >= N)
+        return;
+    if constexpr (DEPTH == 1) {
+        stream_rows<NT, CPL, DEPTH, HOIST>(A, B, Cb, w, r1, nw, N, stride, st, qs, d8, K, y, ldy,
+                                           lane);
+    } else if constexpr (DEPTH == 2) {
+        load_row(A, w, r2, N, stride, st);
+        __builtin_amdgcn_sched_barrier(0);
+        Q6K_FINISH(B, r1);
+        if (r2 >= N)
+            return;
+        stream_rows<NT, CPL, DEPTH, HOIST>(A, B, Cb, w, r2, nw, N, stride, st, qs, d8, K, y, ldy,
+                                           lane);
+    } else {
+        load_row(A, w, r3, N, stride, st);
+        __builtin_amdgcn_sched_barrier(0);
+        Q6K_FINISH(B, r1);
+        if (r2 >= N)
+            return;
+        load_row(B, w, r3 + nw, N, stride, st);
+        __builtin_amdgcn_sched_barrier(0);
+        Q6K_FINISH(Cb, r2);
+        if (r3 >= N)
+            return;
+        stream_rows<NT, CPL, DEPTH, HOIST>(A, B, Cb, w, r3, nw, N, stride, st, qs, d8, K, y, ldy,
+                                           lane);
+    }
+}
 #undef Q6K_FINISH
+
+// Rows with at most MAX_CPL chunks per lane; DEPTH rows in flight per wave.
+template <int NT, int CPL, int DEPTH, bool HOIST>
+__global__ __launch_bounds__(WG) void mmvq_rows(const uint8_t *__restrict__ w,
+                                                const int8_t *__restrict__ qs,
+                                                const uint16_t *__restrict__ d8,
+                                                float *__restrict__ y, uint32_t N, uint32_t nbe,
+                                                uint32_t stride, uint32_t K, uint32_t ldy)
+{
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = blockIdx.x * WAVES_PER_WG + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t nw = gridDim.x * WAVES_PER_WG;
+    LaneState<NT, CPL, HOIST> st;
+    lane_init(st, lane, nbe, qs, d8, K);
+    if (wave >= N)
+        return;
+    ChunkW A[CPL], B[CPL], Cb[CPL];
+    prime_rows<NT, CPL, 0, DEPTH - 1, HOIST>(A, B, Cb, w, wave, nw, N, stride, st);
+    stream_rows<NT, CPL, DEPTH, HOIST>(A, B, Cb, w, wave, nw, N, stride, st, qs, d8, K, y, ldy,
+                                       lane);
+}
+
+// RMSNorm -> q8 -> GEMV in one kernel, for the shapes whose activation operands
+// stay in registers. Every workgroup normalizes and quantizes the NT activation
+// rows itself, into LDS, with the RMSNorm -> q8 producer's own body and order
+// (q6k_norm.h), so its operands equal that producer's q8 plane bit for bit and the
+// outputs equal those of the producer followed by the GEMV. Workgroup 0 also
+// stores the q8 plane and, when xn is not null, the normalized rows. The weight
+// rows do not depend on the activations: a wave requests its first rows right
+// after its activation loads, so the weight stream is under way while the norm runs (the activation loads are issued first, so waiting for them does not
+// wait for the weights). The re-reads of x (K * 4 B per token and workgroup) hit
+// L2 after the first workgroup of each die.
+template <int NT, int CPL, int DEPTH>
+__global__ __launch_bounds__(WG) void mmvq_rmsnorm_rows(
+    const uint8_t *__restrict__ w, const float4 *__restrict__ x, const float4 *__restrict__ gamma,
+    float eps, float4 *__restrict__ xn, uint32_t *__restrict__ qs_out,
+    uint16_t *__restrict__ d8_out, float *__restrict__ y, uint32_t N, uint32_t nbe,
+    uint32_t stride, uint32_t K, uint32_t ldy)
+{
+    static_assert(WG == NORM_WG, "the norm body assumes one 256-thread workgroup");
+    constexpr int VPT = 2 * CPL;               // NORM_WG * VPT float4s >= K / 4 = 64 * nbe
+    constexpr int K4_MAX = NORM_WG * VPT;
+    // rows requested before the norm: all DEPTH, unless x, gamma and the weight
+    // buffers would pass about 200 registers while the norm runs (two workgroups per
+    // CU, DEPTH 2, leave 256 per lane); then the last one after it
+    constexpr int PRE = (DEPTH == 2 && CPL * (8 * NT + 8 + 22) > 200) ? DEPTH - 1 : DEPTH;
+    __shared__ __align__(16) uint32_t s_qs[NT][K4_MAX];
+    __shared__ __align__(16) uint16_t s_d8[NT][K4_MAX / 8];
+    __shared__ double part[NT * (NORM_WG / 64)];
+
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = blockIdx.x * WAVES_PER_WG + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t nw = gridDim.x * WAVES_PER_WG;
+    const uint32_t K4 = K / 4u;
+
+    // buffer loads with a per-row extent of K4 float4s: past the end they return
+    // zeros, which the norm body expects there
+    float4 xv[NT][VPT], gv[VPT];
+    {
+        const __amdgpu_buffer_rsrc_t rg = f4_desc(gamma, K4);
+        __amdgpu_buffer_rsrc_t rx[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            rx[t] = f4_desc(x + (size_t)t * K4, K4);
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const uint32_t f = threadIdx.x + v * NORM_WG;
+            gv[v] = load_f4(rg, f);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                xv[t][v] = load_f4(rx[t], f);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    LaneState<NT, CPL, true> st;
+    lane_chunks(st, lane, nbe);
+    ChunkW A[CPL], B[CPL], Cb[CPL];
+    // a wave with no row primes empty descriptors (no memory traffic); it still
+    // takes part in the workgroup's norm below
+    prime_rows<NT, CPL, 0, PRE, true>(A, B, Cb, w, wave, nw, N, stride, st);
+    __builtin_amdgcn_sched_barrier(0);
+
+    const bool store = blockIdx.x == 0;
+    norm_quant_rows<NT, VPT>(xv, gv, K, eps, part,
+                             [&](int t, uint32_t f, float4 yv, const Q8Out &o) {
+                                 s_qs[t][f] = o.packed;
+                                 if ((f & 7u) == 0)
+                                     s_d8[t][f >> 3] = o.d16;
+                                 if (store) {
+                                     if (xn)
+                                         xn[(size_t)t * K4 + f] = yv;
+                                     qs_out[(size_t)t * K4 + f] = o.packed;
+                                     if ((f & 7u) == 0)
+                                         d8_out[(size_t)t * (K / 32u) + (f >> 3)] = o.d16;
+                                 }
+                             });
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            st.act[i][t] = load_act(reinterpret_cast<const int8_t *>(&s_qs[t][0]), &s_d8[t][0],
+                                    st.Q[i]);
+    }
+    if (wave >= N)
+        return;
+    prime_rows<NT, CPL, PRE, DEPTH, true>(A, B, Cb, w, wave, nw, N, stride, st);
+    __builtin_amdgcn_sched_barrier(0);
+    stream_rows_primed<NT, CPL, DEPTH, true>(A, B, Cb, w, wave, nw, N, stride, st, nullptr,
+                                             nullptr, K, y, ldy, lane);
 }
 
 // Any row length: a row is walked in steps of STEP chunks per lane.
@@ -334,7 +530,7 @@ __global__ __launch_bounds__(WG) void mmvq_long(const uint8_t *__restrict__ w,
                 for (int t = 0; t < NT; ++t) {
                     const ChunkAct a =
                         load_act(qs + (size_t)t * K, d8 + (size_t)t * (K / 32), Qs[i]);
-                    acc[t] += chunk_partial_d(wt[i], a, Qs[i], d);
+                    acc[t] = chunk_accumulate(acc[t], wt[i], a, Qs[i], d);
                 }
             }
         }
@@ -444,6 +640,63 @@ hipError_t dispatch_cpl(int cpl, const RowsCfg &c, std::integer_sequence<int, CP
     return e;
 }
 
+// The fused RMSNorm -> q8 -> GEMV kernel is used for one token whose activation
+// operands stay in registers (up to 6 chunks per lane, K <= 12288). With more
+// tokens the norm work in every workgroup's prologue (one token's worth per token)
+// is no longer hidden behind the first weight rows, and the producer kernel
+// followed by the GEMV measured faster on lm_head 152064 x 5120 (nt = 2: equal;
+// nt = 3, 4: 2 and 4 us faster), so those shapes take the two kernels (with the
+// same results bit for bit).
+constexpr bool fused_ok(int nt, int cpl)
+{
+    return nt == 1 && cpl >= 1 && cpl <= 6;
+}
+
+struct FusedArgs {
+    const uint8_t *w;
+    const float4 *x, *gamma;
+    float eps;
+    float4 *xn;
+    uint32_t *qs;
+    uint16_t *d8;
+    float *y;
+    uint32_t N, nbe, stride, K, ldy;
+};
+
+template <int NT, int CPL>
+hipError_t launch_fused_cpl(int depth, uint32_t grid, hipStream_t s, FusedArgs a)
+{
+    if constexpr (fused_ok(NT, CPL)) {
+        void *args[] = {(void *)&a.w, (void *)&a.x, (void *)&a.gamma, (void *)&a.eps,
+                        (void *)&a.xn, (void *)&a.qs, (void *)&a.d8, (void *)&a.y,
+                        (void *)&a.N, (void *)&a.nbe, (void *)&a.stride, (void *)&a.K,
+                        (void *)&a.ldy};
+        // the (depth, hoist) pair rows_cfg picks for this NT * CPL
+        const void *kern = nullptr;
+        if constexpr (NT * CPL <= 3) {
+            if (depth == 3)
+                kern = (const void *)mmvq_rmsnorm_rows<NT, CPL, 3>;
+        } else {
+            if (depth == 2)
+                kern = (const void *)mmvq_rmsnorm_rows<NT, CPL, 2>;
+        }
+        if (kern)
+            return hipLaunchKernel(kern, dim3(grid), dim3(WG), args, 0, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int NT, int... CPLS>
+hipError_t dispatch_fused(int cpl, int depth, std::integer_sequence<int, CPLS...>, uint32_t grid,
+                          hipStream_t s, const FusedArgs &a)
+{
+    hipError_t e = hipErrorInvalidValue;
+    (void)((cpl == CPLS + 1 ? (e = launch_fused_cpl<NT, CPLS + 1>(depth, grid, s, a), true)
+                            : false) ||
+           ...);
+    return e;
+}
+
 // Workgroups: whole multiples of the CU count (an uneven count leaves some CUs one
 // workgroup short), never more waves than rows.
 uint32_t grid_for(int64_t N, int num_cu, int wg_per_cu)
@@ -508,6 +761,46 @@ hipError_t launch_mmvq(const uint8_t *w, const uint8_t *q8, float *y, int64_t N,
             return e;
     }
     return hipSuccess;
+}
+
+bool rmsnorm_mmvq_fused(int64_t K, int nt)
+{
+    return fused_ok(nt, (int)((K / 256 * 8 + 63) / 64));
+}
+
+hipError_t launch_rmsnorm_mmvq(const uint8_t *w, const float *x, const float *gamma, float eps,
+                               float *xn, uint8_t *q8, float *y, int64_t N, int64_t K, int nt,
+                               int num_cu, hipStream_t s)
+{
+    if (!rmsnorm_mmvq_fused(K, nt)) {
+        // the producer writes the q8 plane, then the GEMV reads it
+        const hipError_t e = launch_rmsnorm_quant(x, gamma, eps, xn, q8, K, nt, s);
+        if (e != hipSuccess)
+            return e;
+        return launch_mmvq(w, q8, y, N, K, nt, num_cu, s);
+    }
+    const uint32_t nbe = (uint32_t)(K / 256);
+    const uint32_t stride = (uint32_t)(((int64_t)nbe * 210 + 15) & ~(int64_t)15);
+    const int cpl = (int)((8u * nbe + 63u) / 64u);
+    uint32_t *qs = reinterpret_cast<uint32_t *>(q8);
+    uint16_t *d8 = reinterpret_cast<uint16_t *>(q8 + (size_t)nt * K);
+    const RowsCfg c = rows_cfg(1, cpl);
+    const uint32_t grid = grid_for(N, num_cu, c.wg_per_cu);
+    FusedArgs a;
+    a.w = w;
+    a.x = reinterpret_cast<const float4 *>(x);
+    a.gamma = reinterpret_cast<const float4 *>(gamma);
+    a.eps = eps;
+    a.xn = reinterpret_cast<float4 *>(xn);
+    a.qs = qs;
+    a.d8 = d8;
+    a.y = y;
+    a.N = (uint32_t)N;
+    a.nbe = nbe;
+    a.stride = stride;
+    a.K = (uint32_t)K;
+    a.ldy = (uint32_t)N;
+    return dispatch_fused<1>(cpl, c.depth, std::make_integer_sequence<int, 6>{}, grid, s, a);
 }
 
 hipError_t launch_subdots(const uint8_t *w, const uint8_t *q8, int32_t *dots, int64_t N,

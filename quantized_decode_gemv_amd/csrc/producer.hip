@@ -1,58 +1,13 @@
 // producer.hip -- q8 activation producers for gfx950: the standalone quantizer, the
-// fused RMSNorm -> q8 producer and the fused SwiGLU -> q8 producer.
-//
-// The q8 body follows the per-32-block quantizer of D3-5 §3.2: amax = max|x|,
-// d = amax/127 (f32 division), di = d != 0 ? 1/d : 0 (f32 division),
-// q = clamp(rint(x*di), -128, 127) with ties to even, stored scale f16(d).
-// HIP's default f32 division and rintf (v_rndne_f32) are IEEE, and there is no
-// add next to a product to contract, so every byte follows from its own input value
-// and its block's amax (max is exact under any association).
-//
-// Thread geometry: a lane holds 4 consecutive values (one float4), 8 consecutive
-// lanes hold one 32-value block, and the block's amax is a DPP max over those 8
-// lanes (pairs, quads, then mirrored half-rows). Every lane of a wave runs it;
-// lanes past the end carry zeros and store nothing, so no lane leaves before a
-// cross-lane step.
+// fused RMSNorm -> q8 producer and the fused SwiGLU -> q8 producer. The q8 block
+// body, its thread geometry and the RMSNorm body are in q6k_norm.h.
 
 #include "q6k_internal.h"
+#include "q6k_norm.h"
 
 namespace q6k {
 
 namespace {
-
-struct Q8Out {
-    uint32_t packed;   // 4 int8 codes
-    uint16_t d16;      // f16 block scale (meaningful on every lane of the group)
-};
-
-__device__ __forceinline__ int q_of(float v, float di)
-{
-    int q = (int)rintf(v * di);
-    return q < -128 ? -128 : (q > 127 ? 127 : q);
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_max(float v)
-{
-    return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                        0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false)));
-}
-
-// All 64 lanes must call this together; lanes 8m..8m+7 form one block.
-__device__ __forceinline__ Q8Out quant_group8(float4 v)
-{
-    float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    m = dpp_max<0xB1>(m);    // quad_perm [1,0,3,2]: pairs
-    m = dpp_max<0x4E>(m);    // quad_perm [2,3,0,1]: quads
-    m = dpp_max<0x141>(m);   // row_half_mirror: the two quads of each 8 lanes
-    const float d = m / 127.0f;
-    const float di = (d != 0.0f) ? 1.0f / d : 0.0f;
-    Q8Out o;
-    o.packed = (uint32_t)(uint8_t)q_of(v.x, di) | ((uint32_t)(uint8_t)q_of(v.y, di) << 8) |
-               ((uint32_t)(uint8_t)q_of(v.z, di) << 16) | ((uint32_t)(uint8_t)q_of(v.w, di) << 24);
-    o.d16 = __builtin_bit_cast(uint16_t, (_Float16)d);
-    return o;
-}
 
 constexpr int QWG = 256;
 
@@ -100,115 +55,70 @@ __global__ __launch_bounds__(QWG) void swiglu_quant_kernel(const float4 *g, cons
     }
 }
 
-__device__ __forceinline__ double block_sum_f64(double v, double *part, int nwaves)
-{
-    v += __shfl_xor(v, 32);
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 8);
-    v += __shfl_xor(v, 4);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 1);
-    if ((threadIdx.x & 63u) == 0)
-        part[threadIdx.x >> 6] = v;
-    __syncthreads();
-    double tot = 0.0;
-    for (int i = 0; i < nwaves; ++i)    // every thread adds in the same order
-        tot += part[i];
-    return tot;
-}
-
-__device__ __forceinline__ float4 rms_scale(float4 x, float4 g, float r)
-{
-    return make_float4((x.x * r) * g.x, (x.y * r) * g.y, (x.z * r) * g.z, (x.w * r) * g.w);
-}
-
-__device__ __forceinline__ double sq_sum(float4 v)
-{
-    double s = (double)v.x * (double)v.x;
-    s += (double)v.y * (double)v.y;
-    s += (double)v.z * (double)v.z;
-    s += (double)v.w * (double)v.w;
-    return s;
-}
-
-// One workgroup per token row, the whole row held in registers (VPT float4 per
-// thread, K/4 <= BS*VPT). The sum of squares is fp64 (each x^2 is exact in fp64)
-// in a fixed reduction order; r = f32(1 / sqrt(mean + eps)); y = (x*r)*g in f32 is
-// stored and quantized from the same registers (the bytes equal quant_q8 applied
-// to y).
-template <int BS, int VPT>
-__global__ __launch_bounds__(BS) void rmsnorm_quant_regs(const float4 *__restrict__ x,
-                                                         const float4 *__restrict__ g,
-                                                         float eps, float4 *__restrict__ y,
-                                                         uint32_t *__restrict__ qs,
-                                                         uint16_t *__restrict__ d8, uint32_t K)
+// One workgroup of NORM_WG threads per token row. Rows of up to NORM_WG * VPT
+// float4s are held in registers (x and gamma loaded once); longer rows are walked
+// twice from memory, summing in the same order. y is stored (when y is not null)
+// and quantized from registers, so the bytes equal quant_q8 applied to y.
+template <int VPT>
+__global__ __launch_bounds__(NORM_WG) void rmsnorm_quant_regs(const float4 *__restrict__ x,
+                                                              const float4 *__restrict__ g,
+                                                              float eps, float4 *__restrict__ y,
+                                                              uint32_t *__restrict__ qs,
+                                                              uint16_t *__restrict__ d8, uint32_t K)
 {
     const uint32_t t = blockIdx.x;
     const uint32_t K4 = K / 4u;
     const float4 *xr = x + (size_t)t * K4;
     const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 xv[VPT], gv[VPT];
+    float4 xv[1][VPT], gv[VPT];
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
-        const uint32_t f = threadIdx.x + v * BS;
-        xv[v] = f < K4 ? xr[f] : zero;
+        const uint32_t f = threadIdx.x + v * NORM_WG;
+        xv[0][v] = f < K4 ? xr[f] : zero;
         gv[v] = f < K4 ? g[f] : zero;
     }
-    double ss = 0.0;
-#pragma unroll
-    for (int v = 0; v < VPT; ++v)
-        ss += sq_sum(xv[v]);
-    __shared__ double part[BS / 64];
-    const double tot = block_sum_f64(ss, part, BS / 64);
-    const float r = (float)(1.0 / sqrt(tot / (double)K + (double)eps));
-
-    float4 *yr = y + (size_t)t * K4;
+    __shared__ double part[NORM_WG / 64];
+    float4 *yr = y ? y + (size_t)t * K4 : nullptr;
     uint32_t *qr = qs + (size_t)t * K4;
     uint16_t *dr = d8 + (size_t)t * (K / 32u);
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-        const uint32_t f = threadIdx.x + v * BS;
-        const bool live = f < K4;
-        const float4 yv = rms_scale(xv[v], gv[v], r);
-        const Q8Out o = quant_group8(yv);
-        if (live) {
-            yr[f] = yv;
-            qr[f] = o.packed;
-            if ((f & 7u) == 0)
-                dr[f >> 3] = o.d16;
-        }
-    }
+    norm_quant_rows<1, VPT>(xv, gv, K, eps, part,
+                            [&](int, uint32_t f, float4 yv, const Q8Out &o) {
+                                if (yr)
+                                    yr[f] = yv;
+                                qr[f] = o.packed;
+                                if ((f & 7u) == 0)
+                                    dr[f >> 3] = o.d16;
+                            });
 }
 
-// Any row length: the same computation, walking the row twice from memory.
-template <int BS>
-__global__ __launch_bounds__(BS) void rmsnorm_quant_loop(const float4 *__restrict__ x,
-                                                         const float4 *__restrict__ g,
-                                                         float eps, float4 *__restrict__ y,
-                                                         uint32_t *__restrict__ qs,
-                                                         uint16_t *__restrict__ d8, uint32_t K)
+__global__ __launch_bounds__(NORM_WG) void rmsnorm_quant_loop(const float4 *__restrict__ x,
+                                                              const float4 *__restrict__ g,
+                                                              float eps, float4 *__restrict__ y,
+                                                              uint32_t *__restrict__ qs,
+                                                              uint16_t *__restrict__ d8, uint32_t K)
 {
     const uint32_t t = blockIdx.x;
     const uint32_t K4 = K / 4u;
     const float4 *xr = x + (size_t)t * K4;
-    double ss = 0.0;
-    for (uint32_t f = threadIdx.x; f < K4; f += BS)
-        ss += sq_sum(xr[f]);
-    __shared__ double part[BS / 64];
-    const double tot = block_sum_f64(ss, part, BS / 64);
-    const float r = (float)(1.0 / sqrt(tot / (double)K + (double)eps));
+    double ss[1] = {0.0};
+    for (uint32_t f = threadIdx.x; f < K4; f += NORM_WG)
+        ss[0] += sq_sum4(xr[f]);
+    __shared__ double part[NORM_WG / 64];
+    norm_block_sum<1>(ss, part);
+    const float r = norm_factor(ss[0], K, eps);
 
-    float4 *yr = y + (size_t)t * K4;
+    float4 *yr = y ? y + (size_t)t * K4 : nullptr;
     uint32_t *qr = qs + (size_t)t * K4;
     uint16_t *dr = d8 + (size_t)t * (K / 32u);
-    const uint32_t iters = (K4 + BS - 1) / BS;
+    const uint32_t iters = (K4 + NORM_WG - 1) / NORM_WG;
     for (uint32_t it = 0; it < iters; ++it) {
-        const uint32_t f = it * BS + threadIdx.x;
+        const uint32_t f = it * NORM_WG + threadIdx.x;
         const bool live = f < K4;
         const float4 yv = live ? rms_scale(xr[f], g[f], r) : make_float4(0.f, 0.f, 0.f, 0.f);
         const Q8Out o = quant_group8(yv);
         if (live) {
-            yr[f] = yv;
+            if (yr)
+                yr[f] = yv;
             qr[f] = o.packed;
             if ((f & 7u) == 0)
                 dr[f >> 3] = o.d16;
@@ -256,14 +166,15 @@ hipError_t launch_rmsnorm_quant(const float *x, const float *gamma, float eps, f
                     (void *)&qs, (void *)&d8, (void *)&Ku};
     const int64_t K4 = K / 4;
     const void *kern;
-    int bs;
-    if (K4 <= 256 * 2) { kern = (const void *)rmsnorm_quant_regs<256, 2>; bs = 256; }
-    else if (K4 <= 256 * 4) { kern = (const void *)rmsnorm_quant_regs<256, 4>; bs = 256; }
-    else if (K4 <= 256 * 8) { kern = (const void *)rmsnorm_quant_regs<256, 8>; bs = 256; }
-    else if (K4 <= 1024 * 4) { kern = (const void *)rmsnorm_quant_regs<1024, 4>; bs = 1024; }
-    else if (K4 <= 1024 * 8) { kern = (const void *)rmsnorm_quant_regs<1024, 8>; bs = 1024; }
-    else { kern = (const void *)rmsnorm_quant_loop<1024>; bs = 1024; }
-    return hipLaunchKernel(kern, dim3(nt), dim3(bs), args, 0, s);
+    if (K4 <= NORM_WG * 2)
+        kern = (const void *)rmsnorm_quant_regs<2>;
+    else if (K4 <= NORM_WG * 4)
+        kern = (const void *)rmsnorm_quant_regs<4>;
+    else if (K4 <= NORM_WG * 8)
+        kern = (const void *)rmsnorm_quant_regs<8>;
+    else
+        kern = (const void *)rmsnorm_quant_loop;
+    return hipLaunchKernel(kern, dim3(nt), dim3(NORM_WG), args, 0, s);
 }
 
 }  // namespace q6k

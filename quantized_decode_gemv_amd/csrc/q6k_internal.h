@@ -25,6 +25,12 @@ hipError_t launch_mmvq(const uint8_t *w, const uint8_t *q8, float *y, int64_t N,
                        int nt, int num_cu, hipStream_t s);
 hipError_t launch_subdots(const uint8_t *w, const uint8_t *q8, int32_t *dots, int64_t N,
                           int64_t K, int nt, int num_cu, hipStream_t s);
+// RMSNorm -> q8 -> GEMV: one kernel when rmsnorm_mmvq_fused(K, nt), else the
+// producer then the GEMV (same results bit for bit). xn may be null.
+bool rmsnorm_mmvq_fused(int64_t K, int nt);
+hipError_t launch_rmsnorm_mmvq(const uint8_t *w, const float *x, const float *gamma, float eps,
+                               float *xn, uint8_t *q8, float *y, int64_t N, int64_t K, int nt,
+                               int num_cu, hipStream_t s);
 hipError_t launch_quant(const float *x, uint8_t *q8, int64_t K, int nt, hipStream_t s);
 hipError_t launch_rmsnorm_quant(const float *x, const float *gamma, float eps, float *y,
                                 uint8_t *q8, int64_t K, int nt, hipStream_t s);

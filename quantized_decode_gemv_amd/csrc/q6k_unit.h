@@ -125,24 +125,27 @@ __device__ __forceinline__ void chunk_scales(const ChunkW &w, uint32_t Q, int &s
     sb = (int)(int8_t)(uint8_t)(w.sc.y >> bit);
 }
 
-// The chunk's contribution d * (d8a * sa*Da + d8b * sb*Db), with d passed in (the
-// caller may zero it to drop the chunk). |sa| <= 128 and |D| <= 2^16 fit the 24-bit
-// multiplier, and sa*Da, sb*Db are exact integers below 2^23, so their f32
-// conversion is exact.
-__device__ __forceinline__ float chunk_partial_d(const ChunkW &w, const ChunkAct &a, uint32_t Q,
-                                                 float d)
+// The chunk's contribution before its super-block scale, d8a * (sa*Da) + d8b * (sb*Db):
+// one rounded product, then one fused multiply-add. |sa| <= 128 and |D| <= 2^16 fit
+// the 24-bit multiplier, and sa*Da, sb*Db are exact integers below 2^23, so their
+// f32 conversion is exact. Every multiply-add here and in the callers is written out
+// (the library is built without implicit contraction), so all kernels round alike.
+__device__ __forceinline__ float chunk_partial_nod(const ChunkW &w, const ChunkAct &a, uint32_t Q)
 {
     int Da, Db, sa, sb;
     chunk_dots(w, a, Q, Da, Db);
     chunk_scales(w, Q, sa, sb);
     const float fa = (float)__mul24(sa, Da);
     const float fb = (float)__mul24(sb, Db);
-    return d * (a.da * fa + a.db * fb);
+    return __builtin_fmaf(a.da, fa, a.db * fb);
 }
 
-__device__ __forceinline__ float chunk_partial(const ChunkW &w, const ChunkAct &a, uint32_t Q)
+// acc + d * (the chunk's contribution), d passed in (the caller may zero it to drop
+// the chunk).
+__device__ __forceinline__ float chunk_accumulate(float acc, const ChunkW &w, const ChunkAct &a,
+                                                  uint32_t Q, float d)
 {
-    return chunk_partial_d(w, a, Q, f16_bits_to_f32(w.d));
+    return __builtin_fmaf(d, chunk_partial_nod(w, a, Q), acc);
 }
 
 }  // namespace q6k

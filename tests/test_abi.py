@@ -168,3 +168,40 @@ def test_plan_grid_is_whole_cus_or_one_wave_per_row(N, nt):
     p = q.mmvq_plan(N, 5120, nt, 256)
     waves_needed = -(-N // 4)
     assert p["grid"] == waves_needed or (p["grid"] % 256 == 0 and p["grid"] < waves_needed)
+
+
+def test_fused_rmsnorm_mmvq_rejects_bad_arguments():
+    E = 0x50000000
+    f = q.mmvq_q6k_rmsnorm_q8
+    # weights need K % 256 (the producers alone take K % 32)
+    assert _code(f, A, B, C, 1e-6, None, D, E, 4, 288, 1, 0) == E_SHAPE
+    assert _code(f, A, B, C, 1e-6, None, D, E, 0, 256, 1, 0) == E_SHAPE
+    assert _code(f, A, B, C, 1e-6, None, D, E, 4, 256, 0, 0) == E_SHAPE
+    assert _code(f, A, B, C, 1e-6, None, D, E, 4, 256, 257, 0) == E_SHAPE
+    for i in range(3):
+        args = [A, B, C]
+        args[i] = None
+        assert _code(f, *args, 1e-6, None, D, E, 4, 256, 1, 0) == E_NULL
+    assert _code(f, A, B, C, 1e-6, None, None, E, 4, 256, 1, 0) == E_NULL
+    assert _code(f, A, B, C, 1e-6, None, D, None, 4, 256, 1, 0) == E_NULL
+    assert _code(f, A + 8, B, C, 1e-6, None, D, E, 4, 256, 1, 0) == E_ALIGN
+    assert _code(f, A, B, C, 1e-6, E + 0x1000 + 4, D, E, 4, 256, 1, 0) == E_ALIGN
+    assert _code(f, A, B, C, 1e-6, None, D + 2, E, 4, 256, 1, 0) == E_ALIGN
+    # every output against every input and the other outputs; xn optional
+    assert _code(f, A, B, C, 1e-6, None, A + 16, E, 4, 256, 1, 0) == E_ALIAS      # q8 / w
+    assert _code(f, A, B, C, 1e-6, None, D, B + 16, 4, 256, 1, 0) == E_ALIAS      # y / x
+    assert _code(f, A, B, C, 1e-6, C, D, E, 4, 256, 1, 0) == E_ALIAS              # xn / gamma
+    assert _code(f, A, B, C, 1e-6, D - 512, D, E, 4, 256, 1, 0) == E_ALIAS        # xn / q8
+    assert _code(f, A, B, C, 1e-6, None, D, D + 32, 4, 256, 1, 0) == E_ALIAS      # y / q8
+
+
+@pytest.mark.parametrize("nbe", [1, 8, 9, 16, 17, 20, 24, 25, 40, 48, 49, 54, 74, 96, 97, 200])
+@pytest.mark.parametrize("nt", [1, 2, 3, 4, 5, 8, 9])
+def test_fused_rmsnorm_mmvq_shape_rule(nbe, nt):
+    # one kernel for one token with at most 6 low-bit chunks per lane (K <= 12288),
+    # where the GEMV keeps the activation operands in registers
+    K = 256 * nbe
+    expect = nt == 1 and nbe <= 48
+    assert q.rmsnorm_mmvq_fused(1000, K, nt) == expect
+    if expect:
+        assert q.mmvq_plan(1000, K, nt, 256)["hoist"]

@@ -1,4 +1,5 @@
-"""The producer -> GEMV chain captured in a HIP graph and replayed.
+"""The producer -> GEMV chain (and the fused RMSNorm -> q8 -> GEMV call) captured
+in a HIP graph and replayed.
 
 The library queues plain kernel launches on the caller's stream (no allocation,
 no memset, no synchronisation), so torch's graph capture records them. Every
@@ -28,6 +29,10 @@ def _buffers(producer, K, nt):
 
 
 def _step(producer, b, W, y, N, K, nt):
+    if producer == "fused":
+        q.mmvq_q6k_rmsnorm_q8(W, b["x"], b["gamma"], q6ksynth.RMS_EPS, b["yn"], b["plane"], y,
+                              N, K, nt)
+        return
     if producer == "rmsnorm":
         q.rmsnorm_quant_q8(b["x"], b["gamma"], q6ksynth.RMS_EPS, b["yn"], b["plane"], K, nt)
     elif producer == "swiglu":
@@ -49,7 +54,8 @@ def _fill(producer, b, K, nt, seed):
 
 @pytest.mark.parametrize("producer,N,K,nt", [("rmsnorm", 4096, 5120, 1), ("rmsnorm", 2048, 5120, 4),
                                              ("swiglu", 1024, 13824, 1), ("quant", 64, 1024, 2),
-                                             ("quant", 333, 256 * 97, 5)])
+                                             ("quant", 333, 256 * 97, 5),
+                                             ("fused", 4096, 5120, 1), ("fused", 1024, 5120, 2)])
 def test_graph_replays_match_eager(producer, N, K, nt):
     raw = q6ksynth.raw_q6k(N, K, seed=N + K)
     W = dpl_from_raw(raw, N, K)
