@@ -174,7 +174,10 @@ def main() -> int:
     plane = torch.empty(q.q8_plane_bytes(K, nt), dtype=torch.uint8, device=dev)
     y = torch.empty((nt, N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
-    fused = args.path == "fused" and w.producer == "rmsnorm"
+    # the fused call runs as one kernel only for the shapes the library fuses (one
+    # token); elsewhere it would queue the same two kernels as the split step
+    fused = (args.path == "fused" and w.producer == "rmsnorm"
+             and q.rmsnorm_mmvq_fused(N, K, nt))
 
     def produce(st):
         if w.producer == "rmsnorm":
