@@ -163,13 +163,16 @@ def main() -> int:
     del raw_d
     Ws = [W0] + [W0.clone() for _ in range(copies - 1)]
 
-    x = q6ksynth.activations(w, nt)
     g = q6ksynth.gamma(K, q6ksynth.gamma_seed(w))
-    x_d = torch.from_numpy(x).to(dev)
     g_d = torch.from_numpy(g).to(dev)
-    gate, up = q6ksynth.swiglu_pairs(w, nt)
-    gate_d = torch.from_numpy(gate).to(dev)
-    up_d = torch.from_numpy(up).to(dev)
+    x = gate = up = x_d = gate_d = up_d = None
+    if w.producer == "swiglu":
+        gate, up = q6ksynth.swiglu_pairs(w, nt)
+        gate_d = torch.from_numpy(gate).to(dev)
+        up_d = torch.from_numpy(up).to(dev)
+    else:
+        x = q6ksynth.activations(w, nt)
+        x_d = torch.from_numpy(x).to(dev)
     y_norm = torch.empty((nt, K), dtype=torch.float32, device=dev)
     plane = torch.empty(q.q8_plane_bytes(K, nt), dtype=torch.uint8, device=dev)
     y = torch.empty((nt, N), dtype=torch.float32, device=dev)

@@ -51,3 +51,37 @@ def q8_cases():
         elif tag == "d16":
             cur["d16"] = int(vals[0], 16)
     return [(c["name"], c["x"], c["q"], c["d16"]) for c in cases]
+
+
+def kq_layout():
+    """-> {"block": {type: dict}, "plane": {type: dict}} (offsets; None where absent)."""
+    out = {"block": {}, "plane": {}}
+    conv = lambda v: None if v == "-" else int(v)  # noqa: E731
+    for line in _lines("kq_layout.txt"):
+        kind, name, *vals = line.split()
+        v = [conv(a) for a in vals]
+        if kind == "block":
+            out["block"][name] = dict(bytes=v[0], d=v[1], dmin=v[2], scales=v[3], fifth=v[4],
+                                      codes=v[5])
+        else:
+            out["plane"][name] = dict(codes=v[0], fifth=v[1], scales=v[2], dm=v[3], stride=v[4])
+    return out
+
+
+def kq_code_addressing():
+    rows = []
+    for line in _lines("kq_code_addressing.txt"):
+        s, first, win, nib, fb = line.split()
+        rows.append(dict(s=int(s), first=int(first), window=int(win), nibble=nib,
+                         fifth_bit=int(fb)))
+    return rows
+
+
+def kq_scale_bits():
+    """-> list of (byte, bit, field, sub_block, dst_bit), one per packed bit."""
+    out = []
+    for line in _lines("kq_scale_bits.txt"):
+        byte, lo, hi, field, sub, dst = line.split()
+        for k in range(int(lo), int(hi) + 1):
+            out.append((int(byte), k, field, int(sub), int(dst) + k - int(lo)))
+    return out

@@ -19,8 +19,9 @@ def _chain(w: q6ksynth.Workload, nt: int):
     and on the oracle (repack-free raw rows, producer, GEMV), from the same seeds."""
     raw = q6ksynth.weights(w)
     dpl = dpl_from_raw(raw, w.N, w.K)
-    x = q6ksynth.activations(w, nt)
     plane = q8_plane(w.K, nt)
+    if w.producer != "swiglu":
+        x = q6ksynth.activations(w, nt)
     if w.producer == "rmsnorm":
         g = q6ksynth.gamma(w.K, q6ksynth.gamma_seed(w))
         yd = torch.empty((nt, w.K), dtype=torch.float32, device=DEV)
@@ -77,7 +78,7 @@ def test_subdots_bit_exact(N, K, nt):
     say(f"subdots N={N} K={K} nt={nt}")
     raw = q6ksynth.raw_q6k(N, K, seed=N * 7 + nt)
     dpl = dpl_from_raw(raw, N, K)
-    x = np.stack([q6ksynth.activation("swiglu", K, 900 + c) for c in range(nt)])
+    x = np.stack([oracle.swiglu(*q6ksynth.swiglu_pair(K, 900 + c))[0] for c in range(nt)])
     qs, d = oracle.quant_q8(x)
     plane = make_plane(qs, d)
     dots = torch.zeros((nt, N, K // 16), dtype=torch.int32, device=DEV)

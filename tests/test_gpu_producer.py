@@ -54,7 +54,10 @@ def test_quant_q8_closed_form(case):
 @pytest.mark.parametrize("nt", [1, 4, 5])
 @pytest.mark.parametrize("kind", ["normal", "outlier", "swiglu"])
 def test_quant_q8_bit_exact(K, nt, kind):
-    x = np.stack([q6ksynth.activation(kind, K, 500 + c) for c in range(nt)])
+    if kind == "swiglu":   # SwiGLU-shaped rows (the oracle's silu(g) * u)
+        x = np.stack([oracle.swiglu(*q6ksynth.swiglu_pair(K, 500 + c))[0] for c in range(nt)])
+    else:
+        x = np.stack([q6ksynth.activation(kind, K, 500 + c) for c in range(nt)])
     plane = q8_plane(K, nt)
     q.quant_q8(dev_f32(x), plane, K, nt)
     qs, d = split_plane(plane, K, nt)
