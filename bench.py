@@ -36,10 +36,12 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 PAGES_LM_HEAD_GBS = 250.0       # the pages' dpl lm_head content rate (GB10; context only)
 ROTATE_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mmvq_lm_head_traffic.txt")
+TYPE_NAMES = {12: "q4_K", 13: "q5_K", 14: "q6_K"}
 PRODUCER_NAMES = {"rmsnorm": "fused RMSNorm->q8", "swiglu": "fused SwiGLU->q8",
                   "quant": "q8"}
 KERNEL_SOURCES = [os.path.join(ROOT, "quantized_decode_gemv_amd", "csrc", f)
-                  for f in ("mmvq.hip", "q6k_unit.h", "q6k_norm.h")]
+                  for f in ("mmvq.hip", "q6k_unit.h", "q6k_norm.h", "kq_unit.h", "kq_format.h",
+                            "bufload.h")]
 
 
 def log(*a):
@@ -98,18 +100,25 @@ def cpu_baseline(w, raw, x, g, gate, up, nt: int, budget_s: float = 20.0) -> dic
     else:
         xn = x
     qs, d = oracle.quant_q8(xn)
-    probe = 2048
+
+    def gemv(n):
+        if w.qtype == q6ksynth.Q6_K:
+            oracle.mmvq(oracle.RAW, raw[:n], n, w.K, qs, d, nthreads=1)
+        else:
+            oracle.kq_mmvq(w.qtype, oracle.RAW, raw[:n], n, w.K, qs, d, nthreads=1)
+
+    probe = min(2048, w.N)
     t0 = time.perf_counter()
-    oracle.mmvq(oracle.RAW, raw[:probe], probe, w.K, qs, d, nthreads=1)
+    gemv(probe)
     per_row = (time.perf_counter() - t0) / probe
     rows = int(min(w.N, max(probe, budget_s / 3 / per_row)))
     times = []
     for _ in range(3):
         t0 = time.perf_counter()
-        oracle.mmvq(oracle.RAW, raw[:rows], rows, w.K, qs, d, nthreads=1)
+        gemv(rows)
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
-    content = rows * w.nbe * 210
+    content = rows * w.nbe * q6ksynth.KQ_BLOCK_BYTES[w.qtype]
     return {"value": round(content / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"first {rows} of {w.N} rows of the {w.N}x{w.K} matrix, nt={nt}, "
                       f"scalar C oracle GEMV (fp64), single thread, median of 3 runs "
@@ -154,12 +163,13 @@ def main() -> int:
     log(f"bench: {w.name} N={N} K={K} nt={nt} steps={args.steps} warmup={args.warmup}")
 
     raw = q6ksynth.weights(w)
-    dpl_bytes = q.q6k_dpl_bytes(N, K)
+    qt = w.qtype
+    dpl_bytes = q.kq_dpl_bytes(qt, N, K)
     copies = max(2, math.ceil(ROTATE_BYTES / dpl_bytes)) if dpl_bytes < ROTATE_BYTES else 2
     copies = min(copies, 4096)
     raw_d = torch.from_numpy(raw.reshape(-1)).to(dev)
     W0 = torch.empty(dpl_bytes, dtype=torch.uint8, device=dev)
-    q.repack_q6k_dpl(raw_d, W0, N, K)
+    q.repack_kq_dpl(qt, raw_d, W0, N, K)
     del raw_d
     Ws = [W0] + [W0.clone() for _ in range(copies - 1)]
 
@@ -191,11 +201,11 @@ def main() -> int:
             q.quant_q8(x_d, plane, K, nt, st)
 
     def gemv(i, st):
-        q.mmvq_q6k_q8(Ws[i % copies], plane, y, N, K, nt, st)
+        q.mmvq_kq_q8(qt, Ws[i % copies], plane, y, N, K, nt, st)
 
     def fused_call(i, st):
-        q.mmvq_q6k_rmsnorm_q8(Ws[i % copies], x_d, g_d, q6ksynth.RMS_EPS, None, plane, y,
-                              N, K, nt, st)
+        q.mmvq_kq_rmsnorm_q8(qt, Ws[i % copies], x_d, g_d, q6ksynth.RMS_EPS, None, plane, y,
+                             N, K, nt, st)
 
     def split_step(i, st):
         produce(st)
@@ -291,9 +301,11 @@ def main() -> int:
         "vs_baseline": round(value / PAGES_LM_HEAD_GBS, 3) if (w.name == "lm_head" and nt == 1) else None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": f"{w.name} q6_K GEMV N={N} K={K} nt={nt}: "
-                               + (f"RMSNorm->q8->dpl q6_K x q8 MMVQ in one kernel" if fused else
-                                  f"{PRODUCER_NAMES[w.producer]} producer + dpl q6_K x q8 MMVQ"),
+        "config": {"workload": f"{w.name} {TYPE_NAMES[qt]} GEMV N={N} K={K} nt={nt}: "
+                               + (f"RMSNorm->q8->split-plane {TYPE_NAMES[qt]} x q8 MMVQ in one "
+                                  f"kernel" if fused else
+                                  f"{PRODUCER_NAMES[w.producer]} producer + split-plane "
+                                  f"{TYPE_NAMES[qt]} x q8 MMVQ"),
                    "N": N, "K": K, "nt": nt, "content_bytes": content,
                    "dpl_bytes": dpl_bytes, "weight_copies": copies},
         "dominant_kernel": "mmvq_rmsnorm_rows (fused)" if fused else "mmvq_rows",

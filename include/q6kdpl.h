@@ -1,7 +1,7 @@
 /*
  * q6kdpl.h -- C ABI of libq6kdpl.so: the q6_K x q8 batch-1 decode GEMV (MMVQ) over
- * the dense split-plane ("dpl") row layout, and its q8 activation producers, for
- * AMD MI355X (gfx950).
+ * the dense split-plane ("dpl") row layout, its sibling q4_K and q5_K classes over
+ * the same kind of row, and the q8 activation producers, for AMD MI355X (gfx950).
  *
  * Sources (page titles; sections cited at each entry point):
  *   [D4-4] "76 · D4-4 -- the endgame kernel session: dpl dense split-plane q6_K
@@ -43,6 +43,13 @@
  *    sections start 16-B aligned when the plane does. Size q8_plane_bytes(K, nt).
  *  y: float32 [nt][N], y[t*N + r] (the reduction writes output[t*od + row],
  *    [D4-2] §3.2 Excerpt B).
+ *  q4_K / q5_K (the kq_* entry points; the pages name these classes but print no
+ *    layout, so the blocks are the public GGUF definitions): raw super-blocks of
+ *    144 B (q4_K: fp16 d, fp16 dmin, 12 bytes packing eight 6-bit scales and eight
+ *    6-bit mins, 128 bytes of 4-bit codes) or 176 B (q5_K: the same with 32 bytes of
+ *    fifth code bits before the codes); weight value d*sc*q - dmin*m per 32-element
+ *    sub-block. Split-plane row: [codes nbe*128]([fifth bits nbe*32])[scales
+ *    nbe*12][(d, dmin) nbe*4], stride nbe*144 or nbe*176 (already multiples of 16).
  */
 #ifndef Q6KDPL_H
 #define Q6KDPL_H
@@ -60,6 +67,12 @@ extern "C" {
 #define Q6K_E_ALIGN (-3) /* a pointer is not 16-byte aligned                            */
 #define Q6K_E_ALIAS (-4) /* an output byte range overlaps an input byte range           */
 #define Q6K_E_HIP (-5)   /* the HIP runtime refused a launch or a device query          */
+#define Q6K_E_TYPE (-6)  /* unknown weight type                                         */
+
+/* Weight types of the kq_* entry points (GGUF type ids). */
+#define KQ_Q4_K 12
+#define KQ_Q5_K 13
+#define KQ_Q6_K 14
 
 #define Q6K_MAX_N ((int64_t)1 << 30)
 #define Q6K_MAX_K ((int64_t)1 << 20)
@@ -161,8 +174,61 @@ int q6k_rmsnorm_mmvq_fused(int64_t N, int64_t K, int nt);
 int mmvq_q6k_q8_subdots(const void *w_dpl, const void *q8, int32_t *dots, int64_t N, int64_t K,
                         int nt, void *stream);
 
-/* Diagnostics: how mmvq_q6k_q8 runs a shape on a device with num_cu compute units.
- * out6[0] = workgroups per launch (256 threads each), out6[1] = low-bit chunks per
+/* ---- q4_K / q5_K (and q6_K) by weight type ------------------------------------- */
+/* Every kq_* entry takes `type` (KQ_Q4_K, KQ_Q5_K or KQ_Q6_K; anything else is
+ * Q6K_E_TYPE) and otherwise behaves as its q6_K counterpart above, which it equals
+ * for KQ_Q6_K. The q4_K and q5_K classes are the siblings of the q6_K one on the
+ * same decode step ([D4-2] §1 and §2: the q4_K class's stream rate is the bar the
+ * q6_K work is measured against; [D3-5] §3.2: the three MMVQ entries q4_K/q5_K/q6_K
+ * take the same q8 activation plane). */
+
+/* Bytes of one super-block of 256 weights (144, 176, 210); 0 for an unknown type. */
+size_t kq_block_bytes(int type);
+
+/* Split-plane row stride, (K/256 * block bytes + 15) & ~15; 0 on a bad type or K. */
+size_t kq_dpl_row_stride(int type, int64_t K);
+
+/* Bytes of a split-plane matrix (N * stride) / of a raw matrix (N * K/256 * block
+ * bytes); 0 on a bad type or shape. */
+size_t kq_dpl_bytes(int type, int64_t N, int64_t K);
+size_t kq_raw_bytes(int type, int64_t N, int64_t K);
+
+/* Host repack raw -> split-plane rows (each block field copied to its plane, the
+ * row tail zeroed) and its inverse; as repack_q6k_dpl_host / unpack_q6k_dpl_host. */
+int repack_kq_dpl_host(int type, const uint8_t *raw, uint8_t *dpl, int64_t N, int64_t K);
+int unpack_kq_dpl_host(int type, const uint8_t *dpl, uint8_t *raw, int64_t N, int64_t K);
+
+/* Device repack, byte-identical to repack_kq_dpl_host; as repack_q6k_dpl. */
+int repack_kq_dpl(int type, const void *raw_dev, void *dpl_dev, int64_t N, int64_t K,
+                  void *stream);
+
+/* The MMVQ over split-plane rows of `type` with the q8 plane of quant_q8 (and the
+ * other producers). q4_K / q5_K: y[t][r] = sum over super-blocks b and 32-element
+ * sub-blocks s of f16(d8_t,8b+s) * (f16(d_rb) * sc_rbs * Dq - f16(dmin_rb) * m_rbs * Sx),
+ * Dq the exact int32 dot of the sub-block's codes with its int8 activations and Sx
+ * the activations' sum; scaling and summation in f32 (error well inside
+ * 1e-5 * sum|terms|, terms counted as the scale and min products). Arguments,
+ * alignment, coverage and errors as mmvq_q6k_q8, with w_dpl of kq_dpl_bytes(type,
+ * N, K) bytes. */
+int mmvq_kq_q8(int type, const void *w_dpl, const void *q8, float *y, int64_t N, int64_t K,
+               int nt, void *stream);
+
+/* RMSNorm -> q8 -> MMVQ for `type`, as mmvq_q6k_rmsnorm_q8 (one kernel where
+ * q6k_rmsnorm_mmvq_fused(N, K, nt) is 1, for every type). */
+int mmvq_kq_rmsnorm_q8(int type, const void *w_dpl, const float *x, const float *gamma,
+                       float eps, float *xn, void *q8, float *y, int64_t N, int64_t K, int nt,
+                       void *stream);
+
+/* Test entry: the exact integer dots of mmvq_kq_q8. KQ_Q6_K: as mmvq_q6k_q8_subdots
+ * (K/16 per row). KQ_Q4_K / KQ_Q5_K: Dq per 32-element sub-block,
+ * dots[(t*N + r)*(K/32) + s] (int32, device, 16-B aligned). */
+int mmvq_kq_q8_subdots(int type, const void *w_dpl, const void *q8, int32_t *dots, int64_t N,
+                       int64_t K, int nt, void *stream);
+
+/* Diagnostics: how mmvq_q6k_q8 (and mmvq_kq_q8, the same for every type) runs a
+ * shape on a device with num_cu compute units.
+ * out6[0] = workgroups per launch (256 threads each; a launch uses fewer where the
+ * kernel's registers fit fewer workgroups per CU), out6[1] = low-bit chunks per
  * lane per row, out6[2] = 1 for a fixed-length kernel (0: the generic stepping
  * kernel), out6[3] = 1 when activation operands stay in registers across rows,
  * out6[4] = launches (one per group of up to 4 token columns), out6[5] = rows in

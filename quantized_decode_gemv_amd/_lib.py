@@ -11,6 +11,7 @@ import torch  # loads the HIP runtime this library then shares (same soname)
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libq6kdpl.so")
 
+KQ_Q4_K, KQ_Q5_K, KQ_Q6_K = 12, 13, 14     # weight types (GGUF type ids)
 Q6K_MAX_N = 1 << 30
 Q6K_MAX_K = 1 << 20
 Q6K_MAX_NT = 256
@@ -38,6 +39,17 @@ _SIGS = {
     "mmvq_q6k_rmsnorm_q8": (_INT, [_P, _P, _P, ctypes.c_float, _P, _P, _P, _I64, _I64, _INT,
                                    _P]),
     "q6k_rmsnorm_mmvq_fused": (_INT, [_I64, _I64, _INT]),
+    "kq_block_bytes": (_SZ, [_INT]),
+    "kq_dpl_row_stride": (_SZ, [_INT, _I64]),
+    "kq_dpl_bytes": (_SZ, [_INT, _I64, _I64]),
+    "kq_raw_bytes": (_SZ, [_INT, _I64, _I64]),
+    "repack_kq_dpl_host": (_INT, [_INT, _P, _P, _I64, _I64]),
+    "unpack_kq_dpl_host": (_INT, [_INT, _P, _P, _I64, _I64]),
+    "repack_kq_dpl": (_INT, [_INT, _P, _P, _I64, _I64, _P]),
+    "mmvq_kq_q8": (_INT, [_INT, _P, _P, _P, _I64, _I64, _INT, _P]),
+    "mmvq_kq_rmsnorm_q8": (_INT, [_INT, _P, _P, _P, ctypes.c_float, _P, _P, _P, _I64, _I64,
+                                  _INT, _P]),
+    "mmvq_kq_q8_subdots": (_INT, [_INT, _P, _P, _P, _I64, _I64, _INT, _P]),
     "q6k_mmvq_plan": (_INT, [_I64, _I64, _INT, _INT, _P]),
 }
 
@@ -216,3 +228,69 @@ def mmvq_plan(N: int, K: int, nt: int, num_cu: int) -> dict:
     _call("q6k_mmvq_plan", N, K, nt, num_cu, ctypes.addressof(out))
     return dict(grid=out[0], cpl=out[1], unrolled=bool(out[2]), hoist=bool(out[3]),
                 launches=out[4], depth=out[5])
+
+
+# --- by weight type (q4_K, q5_K, q6_K) ---------------------------------------------
+
+def kq_block_bytes(qtype: int) -> int:
+    return int(lib().kq_block_bytes(qtype))
+
+
+def kq_dpl_row_stride(qtype: int, K: int) -> int:
+    return int(lib().kq_dpl_row_stride(qtype, K))
+
+
+def kq_dpl_bytes(qtype: int, N: int, K: int) -> int:
+    return int(lib().kq_dpl_bytes(qtype, N, K))
+
+
+def kq_raw_bytes(qtype: int, N: int, K: int) -> int:
+    return int(lib().kq_raw_bytes(qtype, N, K))
+
+
+def repack_kq_dpl_host(qtype: int, raw, dpl, N: int, K: int) -> None:
+    _need("raw", raw, kq_raw_bytes(qtype, N, K), device=False)
+    _need("dpl", dpl, kq_dpl_bytes(qtype, N, K), device=False)
+    _call("repack_kq_dpl_host", qtype, _addr(raw), _addr(dpl), N, K)
+
+
+def unpack_kq_dpl_host(qtype: int, dpl, raw, N: int, K: int) -> None:
+    _need("dpl", dpl, kq_dpl_bytes(qtype, N, K), device=False)
+    _need("raw", raw, kq_raw_bytes(qtype, N, K), device=False)
+    _call("unpack_kq_dpl_host", qtype, _addr(dpl), _addr(raw), N, K)
+
+
+def repack_kq_dpl(qtype: int, raw_dev, dpl_dev, N: int, K: int, stream=None) -> None:
+    _need("raw_dev", raw_dev, kq_raw_bytes(qtype, N, K))
+    _need("dpl_dev", dpl_dev, kq_dpl_bytes(qtype, N, K))
+    _call("repack_kq_dpl", qtype, _addr(raw_dev), _addr(dpl_dev), N, K, _stream(stream))
+
+
+def mmvq_kq_q8(qtype: int, w_dpl, q8, y, N: int, K: int, nt: int, stream=None) -> None:
+    _need("w_dpl", w_dpl, kq_dpl_bytes(qtype, N, K))
+    _need("q8", q8, q8_plane_bytes(K, nt))
+    _need("y", y, 4 * max(N, 0) * max(nt, 0))
+    _call("mmvq_kq_q8", qtype, _addr(w_dpl), _addr(q8), _addr(y), N, K, nt, _stream(stream))
+
+
+def mmvq_kq_rmsnorm_q8(qtype: int, w_dpl, x, gamma, eps: float, xn, q8, y, N: int, K: int,
+                       nt: int, stream=None) -> None:
+    _need("w_dpl", w_dpl, kq_dpl_bytes(qtype, N, K))
+    _need("x", x, 4 * K * max(nt, 0))
+    _need("gamma", gamma, 4 * K)
+    if xn is not None:
+        _need("xn", xn, 4 * K * max(nt, 0))
+    _need("q8", q8, q8_plane_bytes(K, nt))
+    _need("y", y, 4 * max(N, 0) * max(nt, 0))
+    _call("mmvq_kq_rmsnorm_q8", qtype, _addr(w_dpl), _addr(x), _addr(gamma), float(eps),
+          _addr(xn), _addr(q8), _addr(y), N, K, nt, _stream(stream))
+
+
+def mmvq_kq_q8_subdots(qtype: int, w_dpl, q8, dots, N: int, K: int, nt: int,
+                       stream=None) -> None:
+    per_row = K // 16 if qtype == KQ_Q6_K else K // 32
+    _need("w_dpl", w_dpl, kq_dpl_bytes(qtype, N, K))
+    _need("q8", q8, q8_plane_bytes(K, nt))
+    _need("dots", dots, 4 * max(N, 0) * max(nt, 0) * max(per_row, 0))
+    _call("mmvq_kq_q8_subdots", qtype, _addr(w_dpl), _addr(q8), _addr(dots), N, K, nt,
+          _stream(stream))

@@ -8,6 +8,7 @@
 #include <atomic>
 
 #include "../../include/q6kdpl.h"
+#include "kq_format.h"
 #include "q6k_internal.h"
 
 namespace {
@@ -31,6 +32,10 @@ bool act_shape_ok(int64_t K, int nt)
 }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? Q6K_OK : Q6K_E_HIP; }
+
+// Sub-block dots per row written by the subdots test entry: q6_K 16-element
+// sub-blocks, q4_K / q5_K 32-element ones.
+int64_t subdots_per_row(int type, int64_t K) { return type == q6k::KQT_Q6_K ? K / 16 : K / 32; }
 
 constexpr int MAX_DEV = 64;
 std::atomic<int> g_cu_count[MAX_DEV];
@@ -72,32 +77,39 @@ const char *q6k_strerror(int code)
     case Q6K_E_ALIGN: return "a device pointer is not 16-byte aligned";
     case Q6K_E_ALIAS: return "an output range overlaps an input range";
     case Q6K_E_HIP: return "the HIP runtime refused a launch or device query";
+    case Q6K_E_TYPE: return "unknown weight type (KQ_Q4_K, KQ_Q5_K and KQ_Q6_K are taken)";
     default: return "unknown q6kdpl error code";
     }
 }
 
 const char *q6k_version(void) { return "q6kdpl 0.1 gfx950"; }
 
-size_t q6k_dpl_row_stride(int64_t K)
+size_t kq_block_bytes(int type) { return q6k::kq_known(type) ? q6k::kq_block_bytes(type) : 0; }
+
+size_t kq_dpl_row_stride(int type, int64_t K)
 {
-    if (K <= 0 || K > Q6K_MAX_K || K % 256)
+    if (!q6k::kq_known(type) || K <= 0 || K > Q6K_MAX_K || K % 256)
         return 0;
-    return (size_t)(((K / 256) * 210 + 15) & ~(int64_t)15);
+    return (size_t)q6k::kq_row_stride(type, (uint64_t)(K / 256));
 }
 
-size_t q6k_dpl_bytes(int64_t N, int64_t K)
+size_t kq_dpl_bytes(int type, int64_t N, int64_t K)
 {
-    if (!weight_shape_ok(N, K))
+    if (!q6k::kq_known(type) || !weight_shape_ok(N, K))
         return 0;
-    return (size_t)N * q6k_dpl_row_stride(K);
+    return (size_t)N * kq_dpl_row_stride(type, K);
 }
 
-size_t q6k_raw_bytes(int64_t N, int64_t K)
+size_t kq_raw_bytes(int type, int64_t N, int64_t K)
 {
-    if (!weight_shape_ok(N, K))
+    if (!q6k::kq_known(type) || !weight_shape_ok(N, K))
         return 0;
-    return (size_t)N * (size_t)(K / 256) * 210u;
+    return (size_t)N * (size_t)(K / 256) * q6k::kq_block_bytes(type);
 }
+
+size_t q6k_dpl_row_stride(int64_t K) { return kq_dpl_row_stride(KQ_Q6_K, K); }
+size_t q6k_dpl_bytes(int64_t N, int64_t K) { return kq_dpl_bytes(KQ_Q6_K, N, K); }
+size_t q6k_raw_bytes(int64_t N, int64_t K) { return kq_raw_bytes(KQ_Q6_K, N, K); }
 
 size_t q8_plane_bytes(int64_t K, int nt)
 {
@@ -106,42 +118,64 @@ size_t q8_plane_bytes(int64_t K, int nt)
     return (size_t)nt * (size_t)K + (size_t)nt * (size_t)(K / 32) * 2u;
 }
 
-int repack_q6k_dpl_host(const uint8_t *raw, uint8_t *dpl, int64_t N, int64_t K)
+int repack_kq_dpl_host(int type, const uint8_t *raw, uint8_t *dpl, int64_t N, int64_t K)
 {
+    if (!q6k::kq_known(type))
+        return Q6K_E_TYPE;
     if (!weight_shape_ok(N, K))
         return Q6K_E_SHAPE;
     if (!raw || !dpl)
         return Q6K_E_NULL;
-    if (overlap(raw, q6k_raw_bytes(N, K), dpl, q6k_dpl_bytes(N, K)))
+    if (overlap(raw, kq_raw_bytes(type, N, K), dpl, kq_dpl_bytes(type, N, K)))
         return Q6K_E_ALIAS;
-    q6k::repack_host(raw, dpl, N, K);
+    q6k::repack_host(type, raw, dpl, N, K);
     return Q6K_OK;
 }
 
-int unpack_q6k_dpl_host(const uint8_t *dpl, uint8_t *raw, int64_t N, int64_t K)
+int unpack_kq_dpl_host(int type, const uint8_t *dpl, uint8_t *raw, int64_t N, int64_t K)
 {
+    if (!q6k::kq_known(type))
+        return Q6K_E_TYPE;
     if (!weight_shape_ok(N, K))
         return Q6K_E_SHAPE;
     if (!raw || !dpl)
         return Q6K_E_NULL;
-    if (overlap(raw, q6k_raw_bytes(N, K), dpl, q6k_dpl_bytes(N, K)))
+    if (overlap(raw, kq_raw_bytes(type, N, K), dpl, kq_dpl_bytes(type, N, K)))
         return Q6K_E_ALIAS;
-    q6k::unpack_host(dpl, raw, N, K);
+    q6k::unpack_host(type, dpl, raw, N, K);
     return Q6K_OK;
 }
 
-int repack_q6k_dpl(const void *raw_dev, void *dpl_dev, int64_t N, int64_t K, void *stream)
+int repack_kq_dpl(int type, const void *raw_dev, void *dpl_dev, int64_t N, int64_t K,
+                  void *stream)
 {
+    if (!q6k::kq_known(type))
+        return Q6K_E_TYPE;
     if (!weight_shape_ok(N, K))
         return Q6K_E_SHAPE;
     if (!raw_dev || !dpl_dev)
         return Q6K_E_NULL;
     if (!aligned16(dpl_dev))
         return Q6K_E_ALIGN;
-    if (overlap(raw_dev, q6k_raw_bytes(N, K), dpl_dev, q6k_dpl_bytes(N, K)))
+    if (overlap(raw_dev, kq_raw_bytes(type, N, K), dpl_dev, kq_dpl_bytes(type, N, K)))
         return Q6K_E_ALIAS;
-    return from_hip(q6k::launch_repack((const uint8_t *)raw_dev, (uint8_t *)dpl_dev, N, K,
+    return from_hip(q6k::launch_repack(type, (const uint8_t *)raw_dev, (uint8_t *)dpl_dev, N, K,
                                        (hipStream_t)stream));
+}
+
+int repack_q6k_dpl_host(const uint8_t *raw, uint8_t *dpl, int64_t N, int64_t K)
+{
+    return repack_kq_dpl_host(KQ_Q6_K, raw, dpl, N, K);
+}
+
+int unpack_q6k_dpl_host(const uint8_t *dpl, uint8_t *raw, int64_t N, int64_t K)
+{
+    return unpack_kq_dpl_host(KQ_Q6_K, dpl, raw, N, K);
+}
+
+int repack_q6k_dpl(const void *raw_dev, void *dpl_dev, int64_t N, int64_t K, void *stream)
+{
+    return repack_kq_dpl(KQ_Q6_K, raw_dev, dpl_dev, N, K, stream);
 }
 
 int quant_q8(const float *x, void *q8, int64_t K, int nt, void *stream)
@@ -191,9 +225,11 @@ int swiglu_quant_q8(const float *g, const float *u, float *y, void *q8, int64_t 
     return from_hip(q6k::launch_swiglu_quant(g, u, y, (uint8_t *)q8, K, nt, (hipStream_t)stream));
 }
 
-int mmvq_q6k_q8(const void *w_dpl, const void *q8, float *y, int64_t N, int64_t K, int nt,
-                void *stream)
+int mmvq_kq_q8(int type, const void *w_dpl, const void *q8, float *y, int64_t N, int64_t K,
+               int nt, void *stream)
 {
+    if (!q6k::kq_known(type))
+        return Q6K_E_TYPE;
     if (!weight_shape_ok(N, K) || !act_shape_ok(K, nt))
         return Q6K_E_SHAPE;
     if (!w_dpl || !q8 || !y)
@@ -201,19 +237,28 @@ int mmvq_q6k_q8(const void *w_dpl, const void *q8, float *y, int64_t N, int64_t 
     if (!aligned16(w_dpl) || !aligned16(q8) || !aligned16(y))
         return Q6K_E_ALIGN;
     const size_t ny = (size_t)nt * N * 4u;
-    if (overlap(y, ny, w_dpl, q6k_dpl_bytes(N, K)) || overlap(y, ny, q8, q8_plane_bytes(K, nt)))
+    if (overlap(y, ny, w_dpl, kq_dpl_bytes(type, N, K)) || overlap(y, ny, q8, q8_plane_bytes(K, nt)))
         return Q6K_E_ALIAS;
     int cu = 0;
     int rc = cu_count((hipStream_t)stream, &cu);
     if (rc != Q6K_OK)
         return rc;
-    return from_hip(q6k::launch_mmvq((const uint8_t *)w_dpl, (const uint8_t *)q8, y, N, K, nt,
-                                     cu, (hipStream_t)stream));
+    return from_hip(q6k::launch_mmvq(type, (const uint8_t *)w_dpl, (const uint8_t *)q8, y, N, K,
+                                     nt, cu, (hipStream_t)stream));
 }
 
-int mmvq_q6k_rmsnorm_q8(const void *w_dpl, const float *x, const float *gamma, float eps,
-                        float *xn, void *q8, float *y, int64_t N, int64_t K, int nt, void *stream)
+int mmvq_q6k_q8(const void *w_dpl, const void *q8, float *y, int64_t N, int64_t K, int nt,
+                void *stream)
 {
+    return mmvq_kq_q8(KQ_Q6_K, w_dpl, q8, y, N, K, nt, stream);
+}
+
+int mmvq_kq_rmsnorm_q8(int type, const void *w_dpl, const float *x, const float *gamma,
+                       float eps, float *xn, void *q8, float *y, int64_t N, int64_t K, int nt,
+                       void *stream)
+{
+    if (!q6k::kq_known(type))
+        return Q6K_E_TYPE;
     if (!weight_shape_ok(N, K) || !act_shape_ok(K, nt))
         return Q6K_E_SHAPE;
     if (!w_dpl || !x || !gamma || !q8 || !y)
@@ -221,7 +266,7 @@ int mmvq_q6k_rmsnorm_q8(const void *w_dpl, const float *x, const float *gamma, f
     if (!aligned16(w_dpl) || !aligned16(x) || !aligned16(gamma) || !aligned16(q8) ||
         !aligned16(y) || (xn && !aligned16(xn)))
         return Q6K_E_ALIGN;
-    const size_t nw = q6k_dpl_bytes(N, K), nx = (size_t)nt * K * 4u, ng = (size_t)K * 4u;
+    const size_t nw = kq_dpl_bytes(type, N, K), nx = (size_t)nt * K * 4u, ng = (size_t)K * 4u;
     const size_t nq = q8_plane_bytes(K, nt), ny = (size_t)nt * N * 4u;
     // every output against every input and every other output
     const void *in[3] = {w_dpl, x, gamma};
@@ -240,9 +285,15 @@ int mmvq_q6k_rmsnorm_q8(const void *w_dpl, const float *x, const float *gamma, f
     int rc = cu_count((hipStream_t)stream, &cu);
     if (rc != Q6K_OK)
         return rc;
-    return from_hip(q6k::launch_rmsnorm_mmvq((const uint8_t *)w_dpl, x, gamma, eps, xn,
+    return from_hip(q6k::launch_rmsnorm_mmvq(type, (const uint8_t *)w_dpl, x, gamma, eps, xn,
                                              (uint8_t *)q8, y, N, K, nt, cu,
                                              (hipStream_t)stream));
+}
+
+int mmvq_q6k_rmsnorm_q8(const void *w_dpl, const float *x, const float *gamma, float eps,
+                        float *xn, void *q8, float *y, int64_t N, int64_t K, int nt, void *stream)
+{
+    return mmvq_kq_rmsnorm_q8(KQ_Q6_K, w_dpl, x, gamma, eps, xn, q8, y, N, K, nt, stream);
 }
 
 int q6k_rmsnorm_mmvq_fused(int64_t N, int64_t K, int nt)
@@ -252,24 +303,33 @@ int q6k_rmsnorm_mmvq_fused(int64_t N, int64_t K, int nt)
     return q6k::rmsnorm_mmvq_fused(K, nt) ? 1 : 0;
 }
 
-int mmvq_q6k_q8_subdots(const void *w_dpl, const void *q8, int32_t *dots, int64_t N, int64_t K,
-                        int nt, void *stream)
+int mmvq_kq_q8_subdots(int type, const void *w_dpl, const void *q8, int32_t *dots, int64_t N,
+                       int64_t K, int nt, void *stream)
 {
+    if (!q6k::kq_known(type))
+        return Q6K_E_TYPE;
     if (!weight_shape_ok(N, K) || !act_shape_ok(K, nt))
         return Q6K_E_SHAPE;
     if (!w_dpl || !q8 || !dots)
         return Q6K_E_NULL;
     if (!aligned16(w_dpl) || !aligned16(q8) || !aligned16(dots))
         return Q6K_E_ALIGN;
-    const size_t nd = (size_t)nt * N * (K / 16) * 4u;
-    if (overlap(dots, nd, w_dpl, q6k_dpl_bytes(N, K)) || overlap(dots, nd, q8, q8_plane_bytes(K, nt)))
+    const size_t nd = (size_t)nt * N * subdots_per_row(type, K) * 4u;
+    if (overlap(dots, nd, w_dpl, kq_dpl_bytes(type, N, K)) ||
+        overlap(dots, nd, q8, q8_plane_bytes(K, nt)))
         return Q6K_E_ALIAS;
     int cu = 0;
     int rc = cu_count((hipStream_t)stream, &cu);
     if (rc != Q6K_OK)
         return rc;
-    return from_hip(q6k::launch_subdots((const uint8_t *)w_dpl, (const uint8_t *)q8, dots, N, K,
-                                        nt, cu, (hipStream_t)stream));
+    return from_hip(q6k::launch_subdots(type, (const uint8_t *)w_dpl, (const uint8_t *)q8, dots, N,
+                                        K, nt, cu, (hipStream_t)stream));
+}
+
+int mmvq_q6k_q8_subdots(const void *w_dpl, const void *q8, int32_t *dots, int64_t N, int64_t K,
+                        int nt, void *stream)
+{
+    return mmvq_kq_q8_subdots(KQ_Q6_K, w_dpl, q8, dots, N, K, nt, stream);
 }
 
 int q6k_mmvq_plan(int64_t N, int64_t K, int nt, int num_cu, int32_t *out6)

@@ -1,22 +1,25 @@
-// mmvq.hip -- q6_K (dpl rows) x q8 decode GEMV kernels for gfx950, and their shape
-// dispatch.
+// mmvq.hip -- k-quant (split-plane rows) x q8 decode GEMV kernels for gfx950, and
+// their shape dispatch. One row machine serves q6_K, q4_K and q5_K through a format
+// policy F (q6k_unit.h: FmtQ6K; kq_unit.h: FmtQ4K, FmtQ5K) that gives a chunk's byte
+// offsets, its loads, its activation operands and its contribution.
 //
-// What is computed (D4-2 §3.2 Excerpt C, the per-unit accumulation; D4-4 §3.2
+// What is computed, q6_K (D4-2 §3.2 Excerpt C, the per-unit accumulation; D4-4 §3.2
 // Excerpt B, the dpl unit load): y[t][r] = sum over the row's 16-element sub-blocks
 // of d * sc * d8 * D, D the exact int32 dot of (q - 32) with the int8 activations.
+// q4_K / q5_K: y[t][r] = sum over 32-element sub-blocks of d8 * (d * sc * Dq -
+// dmin * m * Sx), Dq the exact code dot and Sx the activation sum.
 //
-// Geometry (one design for every shape):
+// Geometry (one design for every shape and format):
 //  - one wave64 owns one row at a time and walks rows with a stride of the grid's
 //    wave count, so the grid streams neighbouring rows together;
-//  - lane L takes the row's 16-byte low-bit chunks Q = L, L + 64, ... (q6k_unit.h):
-//    each low-bit load instruction is one contiguous 1 KB request, each high-bit
-//    load 512 B (two lanes share a chunk), each scale load 128 B, each d load 16 B;
+//  - lane L takes the row's 16-byte low-bit (code) chunks Q = L, L + 64, ...: each
+//    code load instruction is one contiguous 1 KB request; the other planes' loads
+//    are smaller contiguous requests;
 //  - a lane's byte offsets inside a row are the same for every row, so they are
 //    computed once; each row gets a buffer descriptor whose extent is the row's
-//    bytes, and loads are buffer loads at those offsets. The low/high-bit loads are
+//    bytes, and loads are buffer loads at those offsets. The code planes are read
 //    non-temporal (each weight byte is read once per call); the small scale loads
-//    keep the default policy (each 64-byte line of them is touched by three load
-//    instructions of the same row);
+//    keep the default policy;
 //  - lanes past the row's last chunk load a duplicate of the last chunk and
 //    contribute exactly 0, and a wave's look-ahead past the last row uses an empty
 //    descriptor (its loads return zeros without touching memory), so loads are
@@ -35,9 +38,12 @@
 // units of all rows of any shape it is launched on (D4-2 §2: a dispatch that routes
 // a shape to a kernel covering fewer units silently drops work).
 
+#include <mutex>
+#include <unordered_map>
+
+#include "kq_unit.h"
 #include "q6k_internal.h"
 #include "q6k_norm.h"
-#include "q6k_unit.h"
 
 namespace q6k {
 
@@ -45,63 +51,19 @@ constexpr int WG = 256;             // 4 waves per workgroup
 constexpr int WAVES_PER_WG = WG / 64;
 constexpr int MAX_CPL = 12;         // nbe <= 96 take the fixed-length kernels
 constexpr int MAX_NT_KERNEL = 4;    // token columns per launch (more -> several launches)
-constexpr int POLICY_STREAM = 2;    // buffer-load cache policy: non-temporal
-constexpr int POLICY_DEFAULT = 0;
-constexpr int DESC_WORD3 = 0x00020000;  // raw buffer, 32-bit format fields unused
-
-typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
-
-// Byte offsets of one chunk's operands inside a row.
-struct ChunkOffs {
-    uint32_t ql, qh, sc, d;
-};
-
-__device__ __forceinline__ ChunkOffs chunk_offsets(uint32_t Q, uint32_t nbe)
-{
-    const uint32_t G = Q >> 2;
-    ChunkOffs o;
-    o.ql = 16u * Q;
-    o.qh = 128u * nbe + 16u * (2u * G + (Q & 1u));
-    o.sc = 192u * nbe + 8u * G;
-    o.d = 208u * nbe + 2u * (Q >> 3);
-    return o;
-}
 
 // Descriptor of one row; extent 0 for a look-ahead row past the end, whose loads
 // then return zeros without a memory request.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_desc(const uint8_t *w, uint32_t row,
                                                            uint32_t stride, bool real = true)
 {
-    return __builtin_amdgcn_make_buffer_rsrc((void *)(w + (size_t)row * stride), (short)0,
-                                             real ? (int)stride : 0, DESC_WORD3);
+    return buf_desc(w + (size_t)row * stride, real ? stride : 0u);
 }
 
-__device__ __forceinline__ ChunkW load_chunk(__amdgpu_buffer_rsrc_t r, const ChunkOffs &o)
-{
-    const u32x4v a = __builtin_amdgcn_raw_buffer_load_b128(r, (int)o.ql, 0, POLICY_STREAM);
-    const u32x4v b = __builtin_amdgcn_raw_buffer_load_b128(r, (int)o.qh, 0, POLICY_STREAM);
-    const u32x2v c = __builtin_amdgcn_raw_buffer_load_b64(r, (int)o.sc, 0, POLICY_DEFAULT);
-    const uint16_t d = __builtin_amdgcn_raw_buffer_load_b16(r, (int)o.d, 0, POLICY_DEFAULT);
-    ChunkW w;
-    w.ql = make_uint4(a.x, a.y, a.z, a.w);
-    w.qh = make_uint4(b.x, b.y, b.z, b.w);
-    w.sc = make_uint2(c.x, c.y);
-    w.d = d;
-    return w;
-}
-
-// Descriptor of n float4s; loads past them return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t f4_desc(const float4 *p, uint32_t n)
-{
-    return __builtin_amdgcn_make_buffer_rsrc((void *)p, (short)0, (int)(16u * n), DESC_WORD3);
-}
-
+// float4 f of an n-float4 row through its descriptor (zeros past n).
 __device__ __forceinline__ float4 load_f4(__amdgpu_buffer_rsrc_t r, uint32_t f)
 {
-    const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(16u * f), 0, POLICY_DEFAULT);
-    // elements are copied into plain integers before their bit casts: a bit cast
-    // applied straight to a vector element reads element 0
+    const uint4 v = load_b128<POLICY_DEFAULT>(r, 16u * f);
     const uint32_t a = v.x, b = v.y, c = v.z, d = v.w;
     return make_float4(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b),
                        __builtin_bit_cast(float, c), __builtin_bit_cast(float, d));
@@ -173,16 +135,16 @@ __device__ __forceinline__ bool stores_token(uint32_t lane, uint32_t &t)
 }
 
 // Per-lane state that is the same for every row a wave visits.
-template <int NT, int CPL, bool HOIST>
+template <class F, int NT, int CPL, bool HOIST>
 struct LaneState {
-    ChunkOffs off[CPL];
+    typename F::Offs off[CPL];
     uint32_t Q[CPL];        // chunk index (clamped to the last chunk past the row end)
     bool live[CPL];         // false: duplicate load, contributes 0
-    ChunkAct act[HOIST ? CPL : 1][NT];
+    typename F::Act act[HOIST ? CPL : 1][NT];
 };
 
-template <int NT, int CPL, bool HOIST>
-__device__ __forceinline__ void lane_chunks(LaneState<NT, CPL, HOIST> &st, uint32_t lane,
+template <class F, int NT, int CPL, bool HOIST>
+__device__ __forceinline__ void lane_chunks(LaneState<F, NT, CPL, HOIST> &st, uint32_t lane,
                                             uint32_t nbe)
 {
     const uint32_t C = 8u * nbe;
@@ -191,26 +153,26 @@ __device__ __forceinline__ void lane_chunks(LaneState<NT, CPL, HOIST> &st, uint3
         const uint32_t Q = lane + 64u * i;
         st.live[i] = Q < C;
         st.Q[i] = st.live[i] ? Q : C - 1u;
-        st.off[i] = chunk_offsets(st.Q[i], nbe);
+        st.off[i] = F::offsets(st.Q[i], nbe);
     }
 }
 
 // qs, d8: the activation rows (global memory or LDS), token t at qs + t * K and
 // d8 + t * (K / 32).
-template <int NT, int CPL>
-__device__ __forceinline__ void lane_acts(LaneState<NT, CPL, true> &st, const int8_t *qs,
+template <class F, int NT, int CPL>
+__device__ __forceinline__ void lane_acts(LaneState<F, NT, CPL, true> &st, const int8_t *qs,
                                           const uint16_t *d8, uint32_t K)
 {
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-            st.act[i][t] = load_act(qs + (size_t)t * K, d8 + (size_t)t * (K / 32), st.Q[i]);
+            st.act[i][t] = F::act(qs + (size_t)t * K, d8 + (size_t)t * (K / 32), st.Q[i]);
     }
 }
 
-template <int NT, int CPL, bool HOIST>
-__device__ __forceinline__ void lane_init(LaneState<NT, CPL, HOIST> &st, uint32_t lane,
+template <class F, int NT, int CPL, bool HOIST>
+__device__ __forceinline__ void lane_init(LaneState<F, NT, CPL, HOIST> &st, uint32_t lane,
                                           uint32_t nbe, const int8_t *qs, const uint16_t *d8,
                                           uint32_t K)
 {
@@ -219,21 +181,21 @@ __device__ __forceinline__ void lane_init(LaneState<NT, CPL, HOIST> &st, uint32_
         lane_acts(st, qs, d8, K);
 }
 
-template <int NT, int CPL, bool HOIST>
-__device__ __forceinline__ void load_row(ChunkW (&dst)[CPL], const uint8_t *w, uint32_t row,
-                                         uint32_t N, uint32_t stride,
-                                         const LaneState<NT, CPL, HOIST> &st)
+template <class F, int NT, int CPL, bool HOIST>
+__device__ __forceinline__ void load_row(typename F::W (&dst)[CPL], const uint8_t *w,
+                                         uint32_t row, uint32_t N, uint32_t stride,
+                                         const LaneState<F, NT, CPL, HOIST> &st)
 {
     const bool real = row < N;
     const __amdgpu_buffer_rsrc_t r = row_desc(w, real ? row : 0u, stride, real);
 #pragma unroll
     for (int i = 0; i < CPL; ++i)
-        dst[i] = load_chunk(r, st.off[i]);
+        dst[i] = F::load(r, st.off[i]);
 }
 
-template <int NT, int CPL, bool HOIST>
-__device__ __forceinline__ void finish_row(const ChunkW (&src)[CPL],
-                                           const LaneState<NT, CPL, HOIST> &st,
+template <class F, int NT, int CPL, bool HOIST>
+__device__ __forceinline__ void finish_row(const typename F::W (&src)[CPL],
+                                           const LaneState<F, NT, CPL, HOIST> &st,
                                            const int8_t *qs, const uint16_t *d8, uint32_t K,
                                            float *y, uint32_t ldy, uint32_t row, uint32_t lane)
 {
@@ -243,15 +205,14 @@ __device__ __forceinline__ void finish_row(const ChunkW (&src)[CPL],
         acc[t] = 0.0f;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-        const float d = st.live[i] ? f16_bits_to_f32(src[i].d) : 0.0f;   // 0 drops the chunk
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             if constexpr (HOIST) {
-                acc[t] = chunk_accumulate(acc[t], src[i], st.act[i][t], st.Q[i], d);
+                acc[t] = F::accumulate(acc[t], src[i], st.act[i][t], st.Q[i], st.live[i]);
             } else {
-                const ChunkAct a =
-                    load_act(qs + (size_t)t * K, d8 + (size_t)t * (K / 32), st.Q[i]);
-                acc[t] = chunk_accumulate(acc[t], src[i], a, st.Q[i], d);
+                const typename F::Act a =
+                    F::act(qs + (size_t)t * K, d8 + (size_t)t * (K / 32), st.Q[i]);
+                acc[t] = F::accumulate(acc[t], src[i], a, st.Q[i], st.live[i]);
             }
         }
     }
@@ -263,11 +224,11 @@ __device__ __forceinline__ void finish_row(const ChunkW (&src)[CPL],
 
 // Requests rows FROM .. TO - 1 of a wave's walk (row, row + nw, ...), the first
 // DEPTH of which go to A, B and Cb in that order.
-template <int NT, int CPL, int FROM, int TO, bool HOIST>
-__device__ __forceinline__ void prime_rows(ChunkW (&A)[CPL], ChunkW (&B)[CPL], ChunkW (&Cb)[CPL],
-                                           const uint8_t *w, uint32_t row, uint32_t nw,
-                                           uint32_t N, uint32_t stride,
-                                           const LaneState<NT, CPL, HOIST> &st)
+template <class F, int NT, int CPL, int FROM, int TO, bool HOIST>
+__device__ __forceinline__ void prime_rows(typename F::W (&A)[CPL], typename F::W (&B)[CPL],
+                                           typename F::W (&Cb)[CPL], const uint8_t *w,
+                                           uint32_t row, uint32_t nw, uint32_t N, uint32_t stride,
+                                           const LaneState<F, NT, CPL, HOIST> &st)
 {
     if constexpr (FROM <= 0 && TO > 0)
         load_row(A, w, row, N, stride, st);
@@ -282,17 +243,18 @@ __device__ __forceinline__ void prime_rows(ChunkW (&A)[CPL], ChunkW (&B)[CPL], C
 // row DEPTH - 1 ahead, then reduces the oldest (the loads of a step always come
 // first in the loop body: with the reduction first, the compiler waits for every
 // load at the loop head).
-template <int NT, int CPL, int DEPTH, bool HOIST>
-__device__ __forceinline__ void stream_rows(ChunkW (&A)[CPL], ChunkW (&B)[CPL], ChunkW (&Cb)[CPL],
-                                            const uint8_t *w, uint32_t row, uint32_t nw,
-                                            uint32_t N, uint32_t stride,
-                                            const LaneState<NT, CPL, HOIST> &st, const int8_t *qs,
-                                            const uint16_t *d8, uint32_t K, float *y, uint32_t ldy,
-                                            uint32_t lane)
+template <class F, int NT, int CPL, int DEPTH, bool HOIST>
+__device__ __forceinline__ void stream_rows(typename F::W (&A)[CPL], typename F::W (&B)[CPL],
+                                            typename F::W (&Cb)[CPL], const uint8_t *w,
+                                            uint32_t row, uint32_t nw, uint32_t N,
+                                            uint32_t stride,
+                                            const LaneState<F, NT, CPL, HOIST> &st,
+                                            const int8_t *qs, const uint16_t *d8, uint32_t K,
+                                            float *y, uint32_t ldy, uint32_t lane)
 {
     // look-ahead rows past the end get an empty descriptor (load_row), so every load
     // stays unconditional and their results are never reduced
-#define Q6K_FINISH(BUF, ROW) finish_row<NT, CPL, HOIST>(BUF, st, qs, d8, K, y, ldy, ROW, lane)
+#define Q6K_FINISH(BUF, ROW) finish_row<F, NT, CPL, HOIST>(BUF, st, qs, d8, K, y, ldy, ROW, lane)
     if constexpr (DEPTH == 1) {
         for (; row < N; row += nw) {
             load_row(A, w, row, N, stride, st);
@@ -339,12 +301,13 @@ __device__ __forceinline__ void stream_rows(ChunkW (&A)[CPL], ChunkW (&B)[CPL], 
 
 // The same walk with all DEPTH first rows already requested: one step of the
 // walk peeled off without its first request, then stream_rows from the next row.
-template <int NT, int CPL, int DEPTH, bool HOIST>
-__device__ __forceinline__ void stream_rows_primed(ChunkW (&A)[CPL], ChunkW (&B)[CPL],
-                                                   ChunkW (&Cb)[CPL], const uint8_t *w,
+template <class F, int NT, int CPL, int DEPTH, bool HOIST>
+__device__ __forceinline__ void stream_rows_primed(typename F::W (&A)[CPL],
+                                                   typename F::W (&B)[CPL],
+                                                   typename F::W (&Cb)[CPL], const uint8_t *w,
                                                    uint32_t row, uint32_t nw, uint32_t N,
                                                    uint32_t stride,
-                                                   const LaneState<NT, CPL, HOIST> &st,
+                                                   const LaneState<F, NT, CPL, HOIST> &st,
                                                    const int8_t *qs, const uint16_t *d8,
                                                    uint32_t K, float *y, uint32_t ldy,
                                                    uint32_t lane)
@@ -354,16 +317,16 @@ __device__ __forceinline__ void stream_rows_primed(ChunkW (&A)[CPL], ChunkW (&B)
     if (r1 >= N)
         return;
     if constexpr (DEPTH == 1) {
-        stream_rows<NT, CPL, DEPTH, HOIST>(A, B, Cb, w, r1, nw, N, stride, st, qs, d8, K, y, ldy,
-                                           lane);
+        stream_rows<F, NT, CPL, DEPTH, HOIST>(A, B, Cb, w, r1, nw, N, stride, st, qs, d8, K, y,
+                                              ldy, lane);
     } else if constexpr (DEPTH == 2) {
         load_row(A, w, r2, N, stride, st);
         __builtin_amdgcn_sched_barrier(0);
         Q6K_FINISH(B, r1);
         if (r2 >= N)
             return;
-        stream_rows<NT, CPL, DEPTH, HOIST>(A, B, Cb, w, r2, nw, N, stride, st, qs, d8, K, y, ldy,
-                                           lane);
+        stream_rows<F, NT, CPL, DEPTH, HOIST>(A, B, Cb, w, r2, nw, N, stride, st, qs, d8, K, y,
+                                              ldy, lane);
     } else {
         load_row(A, w, r3, N, stride, st);
         __builtin_amdgcn_sched_barrier(0);
@@ -375,14 +338,14 @@ __device__ __forceinline__ void stream_rows_primed(ChunkW (&A)[CPL], ChunkW (&B)
         Q6K_FINISH(Cb, r2);
         if (r3 >= N)
             return;
-        stream_rows<NT, CPL, DEPTH, HOIST>(A, B, Cb, w, r3, nw, N, stride, st, qs, d8, K, y, ldy,
-                                           lane);
+        stream_rows<F, NT, CPL, DEPTH, HOIST>(A, B, Cb, w, r3, nw, N, stride, st, qs, d8, K, y,
+                                              ldy, lane);
     }
 }
 #undef Q6K_FINISH
 
 // Rows with at most MAX_CPL chunks per lane; DEPTH rows in flight per wave.
-template <int NT, int CPL, int DEPTH, bool HOIST>
+template <class F, int NT, int CPL, int DEPTH, bool HOIST>
 __global__ __launch_bounds__(WG) void mmvq_rows(const uint8_t *__restrict__ w,
                                                 const int8_t *__restrict__ qs,
                                                 const uint16_t *__restrict__ d8,
@@ -392,14 +355,14 @@ __global__ __launch_bounds__(WG) void mmvq_rows(const uint8_t *__restrict__ w,
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = blockIdx.x * WAVES_PER_WG + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t nw = gridDim.x * WAVES_PER_WG;
-    LaneState<NT, CPL, HOIST> st;
+    LaneState<F, NT, CPL, HOIST> st;
     lane_init(st, lane, nbe, qs, d8, K);
     if (wave >= N)
         return;
-    ChunkW A[CPL], B[CPL], Cb[CPL];
-    prime_rows<NT, CPL, 0, DEPTH - 1, HOIST>(A, B, Cb, w, wave, nw, N, stride, st);
-    stream_rows<NT, CPL, DEPTH, HOIST>(A, B, Cb, w, wave, nw, N, stride, st, qs, d8, K, y, ldy,
-                                       lane);
+    typename F::W A[CPL], B[CPL], Cb[CPL];
+    prime_rows<F, NT, CPL, 0, DEPTH - 1, HOIST>(A, B, Cb, w, wave, nw, N, stride, st);
+    stream_rows<F, NT, CPL, DEPTH, HOIST>(A, B, Cb, w, wave, nw, N, stride, st, qs, d8, K, y,
+                                          ldy, lane);
 }
 
 // RMSNorm -> q8 -> GEMV in one kernel, for the shapes whose activation operands
@@ -409,10 +372,11 @@ __global__ __launch_bounds__(WG) void mmvq_rows(const uint8_t *__restrict__ w,
 // outputs equal those of the producer followed by the GEMV. Workgroup 0 also
 // stores the q8 plane and, when xn is not null, the normalized rows. The weight
 // rows do not depend on the activations: a wave requests its first rows right
-// after its activation loads, so the weight stream is under way while the norm runs (the activation loads are issued first, so waiting for them does not
-// wait for the weights). The re-reads of x (K * 4 B per token and workgroup) hit
-// L2 after the first workgroup of each die.
-template <int NT, int CPL, int DEPTH>
+// after its activation loads, so the weight stream is under way while the norm
+// runs (the activation loads are issued first, so waiting for them does not wait
+// for the weights). The re-reads of x (K * 4 B per token and workgroup) hit L2
+// after the first workgroup of each die.
+template <class F, int NT, int CPL, int DEPTH>
 __global__ __launch_bounds__(WG) void mmvq_rmsnorm_rows(
     const uint8_t *__restrict__ w, const float4 *__restrict__ x, const float4 *__restrict__ gamma,
     float eps, float4 *__restrict__ xn, uint32_t *__restrict__ qs_out,
@@ -439,11 +403,11 @@ __global__ __launch_bounds__(WG) void mmvq_rmsnorm_rows(
     // zeros, which the norm body expects there
     float4 xv[NT][VPT], gv[VPT];
     {
-        const __amdgpu_buffer_rsrc_t rg = f4_desc(gamma, K4);
+        const __amdgpu_buffer_rsrc_t rg = buf_desc(gamma, 16u * K4);
         __amdgpu_buffer_rsrc_t rx[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-            rx[t] = f4_desc(x + (size_t)t * K4, K4);
+            rx[t] = buf_desc(x + (size_t)t * K4, 16u * K4);
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
             const uint32_t f = threadIdx.x + v * NORM_WG;
@@ -455,12 +419,12 @@ __global__ __launch_bounds__(WG) void mmvq_rmsnorm_rows(
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    LaneState<NT, CPL, true> st;
+    LaneState<F, NT, CPL, true> st;
     lane_chunks(st, lane, nbe);
-    ChunkW A[CPL], B[CPL], Cb[CPL];
+    typename F::W A[CPL], B[CPL], Cb[CPL];
     // a wave with no row primes empty descriptors (no memory traffic); it still
     // takes part in the workgroup's norm below
-    prime_rows<NT, CPL, 0, PRE, true>(A, B, Cb, w, wave, nw, N, stride, st);
+    prime_rows<F, NT, CPL, 0, PRE, true>(A, B, Cb, w, wave, nw, N, stride, st);
     __builtin_amdgcn_sched_barrier(0);
 
     const bool store = blockIdx.x == 0;
@@ -478,23 +442,25 @@ __global__ __launch_bounds__(WG) void mmvq_rmsnorm_rows(
                                  }
                              });
     __syncthreads();
+    // the activation rows in LDS have the layout of the q8 plane: token t at
+    // s_qs[t] (K bytes) and s_d8[t]
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-            st.act[i][t] = load_act(reinterpret_cast<const int8_t *>(&s_qs[t][0]), &s_d8[t][0],
-                                    st.Q[i]);
+            st.act[i][t] = F::act(reinterpret_cast<const int8_t *>(&s_qs[t][0]), &s_d8[t][0],
+                                  st.Q[i]);
     }
     if (wave >= N)
         return;
-    prime_rows<NT, CPL, PRE, DEPTH, true>(A, B, Cb, w, wave, nw, N, stride, st);
+    prime_rows<F, NT, CPL, PRE, DEPTH, true>(A, B, Cb, w, wave, nw, N, stride, st);
     __builtin_amdgcn_sched_barrier(0);
-    stream_rows_primed<NT, CPL, DEPTH, true>(A, B, Cb, w, wave, nw, N, stride, st, nullptr,
-                                             nullptr, K, y, ldy, lane);
+    stream_rows_primed<F, NT, CPL, DEPTH, true>(A, B, Cb, w, wave, nw, N, stride, st, nullptr,
+                                                nullptr, K, y, ldy, lane);
 }
 
 // Any row length: a row is walked in steps of STEP chunks per lane.
-template <int NT>
+template <class F, int NT>
 __global__ __launch_bounds__(WG) void mmvq_long(const uint8_t *__restrict__ w,
                                                 const int8_t *__restrict__ qs,
                                                 const uint16_t *__restrict__ d8,
@@ -513,7 +479,7 @@ __global__ __launch_bounds__(WG) void mmvq_long(const uint8_t *__restrict__ w,
         for (int t = 0; t < NT; ++t)
             acc[t] = 0.0f;
         for (uint32_t base = 0; base < C; base += 64u * STEP) {
-            ChunkW wt[STEP];
+            typename F::W wt[STEP];
             uint32_t Qs[STEP];
             bool live[STEP];
 #pragma unroll
@@ -521,16 +487,15 @@ __global__ __launch_bounds__(WG) void mmvq_long(const uint8_t *__restrict__ w,
                 const uint32_t Q = base + lane + 64u * i;
                 live[i] = Q < C;
                 Qs[i] = live[i] ? Q : C - 1u;
-                wt[i] = load_chunk(r, chunk_offsets(Qs[i], nbe));
+                wt[i] = F::load(r, F::offsets(Qs[i], nbe));
             }
 #pragma unroll
             for (int i = 0; i < STEP; ++i) {
-                const float d = live[i] ? f16_bits_to_f32(wt[i].d) : 0.0f;
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
-                    const ChunkAct a =
-                        load_act(qs + (size_t)t * K, d8 + (size_t)t * (K / 32), Qs[i]);
-                    acc[t] = chunk_accumulate(acc[t], wt[i], a, Qs[i], d);
+                    const typename F::Act a =
+                        F::act(qs + (size_t)t * K, d8 + (size_t)t * (K / 32), Qs[i]);
+                    acc[t] = F::accumulate(acc[t], wt[i], a, Qs[i], live[i]);
                 }
             }
         }
@@ -538,6 +503,45 @@ __global__ __launch_bounds__(WG) void mmvq_long(const uint8_t *__restrict__ w,
         uint32_t t;
         if (stores_token<NT>(lane, t))
             y[(size_t)t * ldy + row] = s;
+    }
+}
+
+// Test kernel (q4_K / q5_K): the exact code dots Dq of every 32-element sub-block,
+// one wave per row, any row length. Chunks Q and Q ^ 1 (lanes L and L ^ 1) hold the
+// two 16-element halves of the same two sub-blocks; C is a multiple of 8, so both
+// lanes of a pair run the loop together.
+template <bool Q5>
+__global__ __launch_bounds__(WG) void kq_subdots_kernel(const uint8_t *__restrict__ w,
+                                                        const int8_t *__restrict__ qs,
+                                                        const uint16_t *__restrict__ d8,
+                                                        int32_t *__restrict__ dots, uint32_t N,
+                                                        uint32_t nbe, uint32_t stride,
+                                                        uint32_t K, uint32_t nt)
+{
+    using F = FmtKq<Q5>;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = blockIdx.x * WAVES_PER_WG + (threadIdx.x >> 6);
+    const uint32_t nwaves = gridDim.x * WAVES_PER_WG;
+    const uint32_t C = 8u * nbe;
+    const uint32_t nsub = K / 32u;
+    for (uint32_t row = wave; row < N; row += nwaves) {
+        const __amdgpu_buffer_rsrc_t r = row_desc(w, row, stride);
+        for (uint32_t Q = lane; Q < C; Q += 64u) {
+            const KqW wt = F::load(r, F::offsets(Q, nbe));
+            const uint32_t s = 2u * (Q >> 1);   // sub-block of the low-nibble half
+            for (uint32_t t = 0; t < nt; ++t) {
+                const KqAct a = kq_load_act(qs + (size_t)t * K, d8 + (size_t)t * (K / 32), Q);
+                int Da, Db;
+                kq_chunk_dots<Q5>(wt, a, Q, Da, Db);
+                Da += __shfl_xor(Da, 1);
+                Db += __shfl_xor(Db, 1);
+                if ((Q & 1u) == 0) {
+                    int32_t *o = dots + ((size_t)t * N + row) * nsub;
+                    o[s] = Da;
+                    o[s + 1u] = Db;
+                }
+            }
+        }
     }
 }
 
@@ -596,46 +600,77 @@ RowsCfg rows_cfg(int nt, int cpl)
     return {1, false, 2};
 }
 
-template <typename Kern>
-hipError_t launch(Kern kern, uint32_t grid, hipStream_t s, const uint8_t *w, const int8_t *qs,
-                  const uint16_t *d8, float *y, uint32_t N, uint32_t nbe, uint32_t stride,
-                  uint32_t K, uint32_t ldy)
+struct GemvArgs {
+    const uint8_t *w;
+    const int8_t *qs;
+    const uint16_t *d8;
+    float *y;
+    uint32_t N, nbe, stride, K, ldy;
+};
+
+// Workgroups of `kern` that fit on one CU at once (its registers and LDS), from the
+// runtime's occupancy calculator, cached per kernel. Some long-row kernels need more
+// than the 256 registers per lane that two workgroups per CU leave; a grid sized
+// for two would then run in two rounds.
+int wg_fit(const void *kern)
 {
-    void *args[] = {(void *)&w, (void *)&qs, (void *)&d8, (void *)&y, (void *)&N,
-                    (void *)&nbe, (void *)&stride, (void *)&K, (void *)&ldy};
+    static std::mutex mu;
+    static std::unordered_map<const void *, int> cache;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(kern);
+    if (it != cache.end())
+        return it->second;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, WG, 0) != hipSuccess || n < 1)
+        return 0;
+    cache.emplace(kern, n);
+    return n;
+}
+
+// Workgroups: whole multiples of the CU count (an uneven count leaves some CUs one
+// workgroup short), never more waves than rows, at most as many per CU as fit.
+uint32_t grid_for(int64_t N, int num_cu, int wg_per_cu)
+{
+    const int64_t need = (N + WAVES_PER_WG - 1) / WAVES_PER_WG;
+    const int64_t full = (int64_t)num_cu * wg_per_cu;
+    return (uint32_t)(need < full ? need : full);
+}
+
+template <typename Kern>
+hipError_t launch(Kern kern, int num_cu, int wg_per_cu, hipStream_t s, GemvArgs a)
+{
+    const int fit = wg_fit((const void *)kern);
+    if (fit < 1)
+        return hipErrorInvalidValue;
+    const uint32_t grid = grid_for(a.N, num_cu, wg_per_cu < fit ? wg_per_cu : fit);
+    void *args[] = {(void *)&a.w, (void *)&a.qs, (void *)&a.d8, (void *)&a.y, (void *)&a.N,
+                    (void *)&a.nbe, (void *)&a.stride, (void *)&a.K, (void *)&a.ldy};
     return hipLaunchKernel((const void *)kern, dim3(grid), dim3(WG), args, 0, s);
 }
 
-template <int NT, int CPL>
-hipError_t launch_cpl(const RowsCfg &c, uint32_t grid, hipStream_t s, const uint8_t *w,
-                      const int8_t *qs, const uint16_t *d8, float *y, uint32_t N, uint32_t nbe,
-                      uint32_t stride, uint32_t K, uint32_t ldy)
+template <class F, int NT, int CPL>
+hipError_t launch_cpl(const RowsCfg &c, int num_cu, hipStream_t s, const GemvArgs &a)
 {
     // only the (depth, hoist) pairs rows_cfg can pick for this NT * CPL are built
     if constexpr (NT * CPL <= 3) {
         if (c.depth == 3)
-            return launch(mmvq_rows<NT, CPL, 3, true>, grid, s, w, qs, d8, y, N, nbe, stride, K, ldy);
+            return launch(mmvq_rows<F, NT, CPL, 3, true>, num_cu, c.wg_per_cu, s, a);
     } else if constexpr (NT * CPL <= 6 || (CPL <= 3 && NT * CPL <= 12)) {
         if (c.depth == 2)
-            return launch(mmvq_rows<NT, CPL, 2, true>, grid, s, w, qs, d8, y, N, nbe, stride, K, ldy);
+            return launch(mmvq_rows<F, NT, CPL, 2, true>, num_cu, c.wg_per_cu, s, a);
     } else {
         if (c.depth == 1)
-            return launch(mmvq_rows<NT, CPL, 1, false>, grid, s, w, qs, d8, y, N, nbe, stride, K, ldy);
+            return launch(mmvq_rows<F, NT, CPL, 1, false>, num_cu, c.wg_per_cu, s, a);
     }
     return hipErrorInvalidValue;
 }
 
-template <int NT, int... CPLS>
+template <class F, int NT, int... CPLS>
 hipError_t dispatch_cpl(int cpl, const RowsCfg &c, std::integer_sequence<int, CPLS...>,
-                        uint32_t grid, hipStream_t s, const uint8_t *w, const int8_t *qs,
-                        const uint16_t *d8, float *y, uint32_t N, uint32_t nbe, uint32_t stride,
-                        uint32_t K, uint32_t ldy)
+                        int num_cu, hipStream_t s, const GemvArgs &a)
 {
     hipError_t e = hipErrorInvalidValue;
-    (void)((cpl == CPLS + 1 ? (e = launch_cpl<NT, CPLS + 1>(c, grid, s, w, qs, d8, y, N, nbe,
-                                                            stride, K, ldy),
-                               true)
-                            : false) ||
+    (void)((cpl == CPLS + 1 ? (e = launch_cpl<F, NT, CPLS + 1>(c, num_cu, s, a), true) : false) ||
            ...);
     return e;
 }
@@ -663,8 +698,8 @@ struct FusedArgs {
     uint32_t N, nbe, stride, K, ldy;
 };
 
-template <int NT, int CPL>
-hipError_t launch_fused_cpl(int depth, uint32_t grid, hipStream_t s, FusedArgs a)
+template <class F, int NT, int CPL>
+hipError_t launch_fused_cpl(int depth, int num_cu, int wg_per_cu, hipStream_t s, FusedArgs a)
 {
     if constexpr (fused_ok(NT, CPL)) {
         void *args[] = {(void *)&a.w, (void *)&a.x, (void *)&a.gamma, (void *)&a.eps,
@@ -675,35 +710,100 @@ hipError_t launch_fused_cpl(int depth, uint32_t grid, hipStream_t s, FusedArgs a
         const void *kern = nullptr;
         if constexpr (NT * CPL <= 3) {
             if (depth == 3)
-                kern = (const void *)mmvq_rmsnorm_rows<NT, CPL, 3>;
+                kern = (const void *)mmvq_rmsnorm_rows<F, NT, CPL, 3>;
         } else {
             if (depth == 2)
-                kern = (const void *)mmvq_rmsnorm_rows<NT, CPL, 2>;
+                kern = (const void *)mmvq_rmsnorm_rows<F, NT, CPL, 2>;
         }
-        if (kern)
-            return hipLaunchKernel(kern, dim3(grid), dim3(WG), args, 0, s);
+        const int fit = kern ? wg_fit(kern) : 0;
+        if (fit >= 1) {
+            const uint32_t g = grid_for(a.N, num_cu, wg_per_cu < fit ? wg_per_cu : fit);
+            return hipLaunchKernel(kern, dim3(g), dim3(WG), args, 0, s);
+        }
     }
     return hipErrorInvalidValue;
 }
 
-template <int NT, int... CPLS>
-hipError_t dispatch_fused(int cpl, int depth, std::integer_sequence<int, CPLS...>, uint32_t grid,
-                          hipStream_t s, const FusedArgs &a)
+template <class F, int NT, int... CPLS>
+hipError_t dispatch_fused(int cpl, int depth, std::integer_sequence<int, CPLS...>, int num_cu,
+                          int wg_per_cu, hipStream_t s, const FusedArgs &a)
 {
     hipError_t e = hipErrorInvalidValue;
-    (void)((cpl == CPLS + 1 ? (e = launch_fused_cpl<NT, CPLS + 1>(depth, grid, s, a), true)
-                            : false) ||
+    (void)((cpl == CPLS + 1
+                ? (e = launch_fused_cpl<F, NT, CPLS + 1>(depth, num_cu, wg_per_cu, s, a), true)
+                : false) ||
            ...);
     return e;
 }
 
-// Workgroups: whole multiples of the CU count (an uneven count leaves some CUs one
-// workgroup short), never more waves than rows.
-uint32_t grid_for(int64_t N, int num_cu, int wg_per_cu)
+template <class F>
+hipError_t launch_mmvq_fmt(const uint8_t *w, const uint8_t *q8, float *y, int64_t N, int64_t K,
+                           int nt, int num_cu, hipStream_t s)
 {
-    const int64_t need = (N + WAVES_PER_WG - 1) / WAVES_PER_WG;
-    const int64_t full = (int64_t)num_cu * wg_per_cu;
-    return (uint32_t)(need < full ? need : full);
+    const uint32_t nbe = (uint32_t)(K / 256);
+    const int8_t *qs = reinterpret_cast<const int8_t *>(q8);
+    const uint16_t *d8 = reinterpret_cast<const uint16_t *>(q8 + (size_t)nt * K);
+    const int cpl = (int)((8u * nbe + 63u) / 64u);
+    for (int t0 = 0; t0 < nt; t0 += MAX_NT_KERNEL) {
+        const int n = nt - t0 < MAX_NT_KERNEL ? nt - t0 : MAX_NT_KERNEL;
+        GemvArgs a;
+        a.w = w;
+        a.qs = qs + (size_t)t0 * K;
+        a.d8 = d8 + (size_t)t0 * (K / 32);
+        a.y = y + (size_t)t0 * N;
+        a.N = (uint32_t)N;
+        a.nbe = nbe;
+        a.stride = (uint32_t)kq_row_stride(F::TYPE, nbe);
+        a.K = (uint32_t)K;
+        a.ldy = (uint32_t)N;
+        hipError_t e;
+        if (cpl <= MAX_CPL) {
+            const RowsCfg c = rows_cfg(n, cpl);
+            const auto seq = std::make_integer_sequence<int, MAX_CPL>{};
+            switch (n) {
+            case 1: e = dispatch_cpl<F, 1>(cpl, c, seq, num_cu, s, a); break;
+            case 2: e = dispatch_cpl<F, 2>(cpl, c, seq, num_cu, s, a); break;
+            case 3: e = dispatch_cpl<F, 3>(cpl, c, seq, num_cu, s, a); break;
+            default: e = dispatch_cpl<F, 4>(cpl, c, seq, num_cu, s, a); break;
+            }
+        } else {
+            switch (n) {
+            case 1: e = launch(mmvq_long<F, 1>, num_cu, 2, s, a); break;
+            case 2: e = launch(mmvq_long<F, 2>, num_cu, 2, s, a); break;
+            case 3: e = launch(mmvq_long<F, 3>, num_cu, 2, s, a); break;
+            default: e = launch(mmvq_long<F, 4>, num_cu, 2, s, a); break;
+            }
+        }
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+template <class F>
+hipError_t launch_fused_fmt(const uint8_t *w, const float *x, const float *gamma, float eps,
+                            float *xn, uint8_t *q8, float *y, int64_t N, int64_t K, int num_cu,
+                            hipStream_t s)
+{
+    const uint32_t nbe = (uint32_t)(K / 256);
+    const int cpl = (int)((8u * nbe + 63u) / 64u);
+    const RowsCfg c = rows_cfg(1, cpl);
+    FusedArgs a;
+    a.w = w;
+    a.x = reinterpret_cast<const float4 *>(x);
+    a.gamma = reinterpret_cast<const float4 *>(gamma);
+    a.eps = eps;
+    a.xn = reinterpret_cast<float4 *>(xn);
+    a.qs = reinterpret_cast<uint32_t *>(q8);
+    a.d8 = reinterpret_cast<uint16_t *>(q8 + (size_t)K);
+    a.y = y;
+    a.N = (uint32_t)N;
+    a.nbe = nbe;
+    a.stride = (uint32_t)kq_row_stride(F::TYPE, nbe);
+    a.K = (uint32_t)K;
+    a.ldy = (uint32_t)N;
+    return dispatch_fused<F, 1>(cpl, c.depth, std::make_integer_sequence<int, 6>{}, num_cu,
+                                c.wg_per_cu, s, a);
 }
 
 }  // namespace
@@ -723,44 +823,15 @@ MmvqPlan plan_mmvq(int64_t N, int64_t K, int nt, int num_cu)
     return p;
 }
 
-hipError_t launch_mmvq(const uint8_t *w, const uint8_t *q8, float *y, int64_t N, int64_t K,
-                       int nt, int num_cu, hipStream_t s)
+hipError_t launch_mmvq(int type, const uint8_t *w, const uint8_t *q8, float *y, int64_t N,
+                       int64_t K, int nt, int num_cu, hipStream_t s)
 {
-    const uint32_t nbe = (uint32_t)(K / 256);
-    const uint32_t stride = (uint32_t)(((int64_t)nbe * 210 + 15) & ~(int64_t)15);
-    const int8_t *qs = reinterpret_cast<const int8_t *>(q8);
-    const uint16_t *d8 = reinterpret_cast<const uint16_t *>(q8 + (size_t)nt * K);
-    const uint32_t Ku = (uint32_t)K, Nu = (uint32_t)N;
-    const int cpl = (int)((8u * nbe + 63u) / 64u);
-    for (int t0 = 0; t0 < nt; t0 += MAX_NT_KERNEL) {
-        const int n = nt - t0 < MAX_NT_KERNEL ? nt - t0 : MAX_NT_KERNEL;
-        const int8_t *qs_t = qs + (size_t)t0 * K;
-        const uint16_t *d8_t = d8 + (size_t)t0 * (K / 32);
-        float *y_t = y + (size_t)t0 * N;
-        hipError_t e;
-        if (cpl <= MAX_CPL) {
-            const RowsCfg c = rows_cfg(n, cpl);
-            const uint32_t grid = grid_for(N, num_cu, c.wg_per_cu);
-            const auto seq = std::make_integer_sequence<int, MAX_CPL>{};
-            switch (n) {
-            case 1: e = dispatch_cpl<1>(cpl, c, seq, grid, s, w, qs_t, d8_t, y_t, Nu, nbe, stride, Ku, Nu); break;
-            case 2: e = dispatch_cpl<2>(cpl, c, seq, grid, s, w, qs_t, d8_t, y_t, Nu, nbe, stride, Ku, Nu); break;
-            case 3: e = dispatch_cpl<3>(cpl, c, seq, grid, s, w, qs_t, d8_t, y_t, Nu, nbe, stride, Ku, Nu); break;
-            default: e = dispatch_cpl<4>(cpl, c, seq, grid, s, w, qs_t, d8_t, y_t, Nu, nbe, stride, Ku, Nu); break;
-            }
-        } else {
-            const uint32_t grid = grid_for(N, num_cu, 2);
-            switch (n) {
-            case 1: e = launch(mmvq_long<1>, grid, s, w, qs_t, d8_t, y_t, Nu, nbe, stride, Ku, Nu); break;
-            case 2: e = launch(mmvq_long<2>, grid, s, w, qs_t, d8_t, y_t, Nu, nbe, stride, Ku, Nu); break;
-            case 3: e = launch(mmvq_long<3>, grid, s, w, qs_t, d8_t, y_t, Nu, nbe, stride, Ku, Nu); break;
-            default: e = launch(mmvq_long<4>, grid, s, w, qs_t, d8_t, y_t, Nu, nbe, stride, Ku, Nu); break;
-            }
-        }
-        if (e != hipSuccess)
-            return e;
+    switch (type) {
+    case KQT_Q6_K: return launch_mmvq_fmt<FmtQ6K>(w, q8, y, N, K, nt, num_cu, s);
+    case KQT_Q4_K: return launch_mmvq_fmt<FmtQ4K>(w, q8, y, N, K, nt, num_cu, s);
+    case KQT_Q5_K: return launch_mmvq_fmt<FmtQ5K>(w, q8, y, N, K, nt, num_cu, s);
+    default: return hipErrorInvalidValue;
     }
-    return hipSuccess;
 }
 
 bool rmsnorm_mmvq_fused(int64_t K, int nt)
@@ -768,52 +839,48 @@ bool rmsnorm_mmvq_fused(int64_t K, int nt)
     return fused_ok(nt, (int)((K / 256 * 8 + 63) / 64));
 }
 
-hipError_t launch_rmsnorm_mmvq(const uint8_t *w, const float *x, const float *gamma, float eps,
-                               float *xn, uint8_t *q8, float *y, int64_t N, int64_t K, int nt,
-                               int num_cu, hipStream_t s)
+hipError_t launch_rmsnorm_mmvq(int type, const uint8_t *w, const float *x, const float *gamma,
+                               float eps, float *xn, uint8_t *q8, float *y, int64_t N, int64_t K,
+                               int nt, int num_cu, hipStream_t s)
 {
     if (!rmsnorm_mmvq_fused(K, nt)) {
         // the producer writes the q8 plane, then the GEMV reads it
         const hipError_t e = launch_rmsnorm_quant(x, gamma, eps, xn, q8, K, nt, s);
         if (e != hipSuccess)
             return e;
-        return launch_mmvq(w, q8, y, N, K, nt, num_cu, s);
+        return launch_mmvq(type, w, q8, y, N, K, nt, num_cu, s);
     }
-    const uint32_t nbe = (uint32_t)(K / 256);
-    const uint32_t stride = (uint32_t)(((int64_t)nbe * 210 + 15) & ~(int64_t)15);
-    const int cpl = (int)((8u * nbe + 63u) / 64u);
-    uint32_t *qs = reinterpret_cast<uint32_t *>(q8);
-    uint16_t *d8 = reinterpret_cast<uint16_t *>(q8 + (size_t)nt * K);
-    const RowsCfg c = rows_cfg(1, cpl);
-    const uint32_t grid = grid_for(N, num_cu, c.wg_per_cu);
-    FusedArgs a;
-    a.w = w;
-    a.x = reinterpret_cast<const float4 *>(x);
-    a.gamma = reinterpret_cast<const float4 *>(gamma);
-    a.eps = eps;
-    a.xn = reinterpret_cast<float4 *>(xn);
-    a.qs = qs;
-    a.d8 = d8;
-    a.y = y;
-    a.N = (uint32_t)N;
-    a.nbe = nbe;
-    a.stride = stride;
-    a.K = (uint32_t)K;
-    a.ldy = (uint32_t)N;
-    return dispatch_fused<1>(cpl, c.depth, std::make_integer_sequence<int, 6>{}, grid, s, a);
+    switch (type) {
+    case KQT_Q6_K: return launch_fused_fmt<FmtQ6K>(w, x, gamma, eps, xn, q8, y, N, K, num_cu, s);
+    case KQT_Q4_K: return launch_fused_fmt<FmtQ4K>(w, x, gamma, eps, xn, q8, y, N, K, num_cu, s);
+    case KQT_Q5_K: return launch_fused_fmt<FmtQ5K>(w, x, gamma, eps, xn, q8, y, N, K, num_cu, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
-hipError_t launch_subdots(const uint8_t *w, const uint8_t *q8, int32_t *dots, int64_t N,
-                          int64_t K, int nt, int num_cu, hipStream_t s)
+hipError_t launch_subdots(int type, const uint8_t *w, const uint8_t *q8, int32_t *dots,
+                          int64_t N, int64_t K, int nt, int num_cu, hipStream_t s)
 {
     uint32_t nbe = (uint32_t)(K / 256);
-    uint32_t stride = (uint32_t)(((int64_t)nbe * 210 + 15) & ~(int64_t)15);
+    uint32_t stride = (uint32_t)kq_row_stride(type, nbe);
     const int8_t *qs = reinterpret_cast<const int8_t *>(q8);
-    uint32_t grid = grid_for(N, num_cu, 4);
+    const uint16_t *d8 = reinterpret_cast<const uint16_t *>(q8 + (size_t)nt * K);
+    const void *kern = type == KQT_Q6_K  ? (const void *)mmvq_subdots_kernel
+                       : type == KQT_Q5_K ? (const void *)kq_subdots_kernel<true>
+                                          : (const void *)kq_subdots_kernel<false>;
+    const int fit = wg_fit(kern);
+    if (fit < 1)
+        return hipErrorInvalidValue;
+    uint32_t grid = grid_for(N, num_cu, fit < 4 ? fit : 4);
     uint32_t Nu = (uint32_t)N, Ku = (uint32_t)K, ntu = (uint32_t)nt;
-    void *args[] = {(void *)&w, (void *)&qs, (void *)&dots, (void *)&Nu,
+    if (type == KQT_Q6_K) {
+        void *args[] = {(void *)&w, (void *)&qs, (void *)&dots, (void *)&Nu,
+                        (void *)&nbe, (void *)&stride, (void *)&Ku, (void *)&ntu};
+        return hipLaunchKernel(kern, dim3(grid), dim3(WG), args, 0, s);
+    }
+    void *args[] = {(void *)&w, (void *)&qs, (void *)&d8, (void *)&dots, (void *)&Nu,
                     (void *)&nbe, (void *)&stride, (void *)&Ku, (void *)&ntu};
-    return hipLaunchKernel((const void *)mmvq_subdots_kernel, dim3(grid), dim3(WG), args, 0, s);
+    return hipLaunchKernel(kern, dim3(grid), dim3(WG), args, 0, s);
 }
 
 }  // namespace q6k

@@ -21,23 +21,25 @@ struct MmvqPlan {
 
 MmvqPlan plan_mmvq(int64_t N, int64_t K, int nt, int num_cu);
 
-hipError_t launch_mmvq(const uint8_t *w, const uint8_t *q8, float *y, int64_t N, int64_t K,
-                       int nt, int num_cu, hipStream_t s);
-hipError_t launch_subdots(const uint8_t *w, const uint8_t *q8, int32_t *dots, int64_t N,
-                          int64_t K, int nt, int num_cu, hipStream_t s);
+// type: a KqType of kq_format.h (the weight rows are that type's split-plane rows).
+hipError_t launch_mmvq(int type, const uint8_t *w, const uint8_t *q8, float *y, int64_t N,
+                       int64_t K, int nt, int num_cu, hipStream_t s);
+hipError_t launch_subdots(int type, const uint8_t *w, const uint8_t *q8, int32_t *dots,
+                          int64_t N, int64_t K, int nt, int num_cu, hipStream_t s);
 // RMSNorm -> q8 -> GEMV: one kernel when rmsnorm_mmvq_fused(K, nt), else the
 // producer then the GEMV (same results bit for bit). xn may be null.
 bool rmsnorm_mmvq_fused(int64_t K, int nt);
-hipError_t launch_rmsnorm_mmvq(const uint8_t *w, const float *x, const float *gamma, float eps,
-                               float *xn, uint8_t *q8, float *y, int64_t N, int64_t K, int nt,
-                               int num_cu, hipStream_t s);
+hipError_t launch_rmsnorm_mmvq(int type, const uint8_t *w, const float *x, const float *gamma,
+                               float eps, float *xn, uint8_t *q8, float *y, int64_t N, int64_t K,
+                               int nt, int num_cu, hipStream_t s);
 hipError_t launch_quant(const float *x, uint8_t *q8, int64_t K, int nt, hipStream_t s);
 hipError_t launch_rmsnorm_quant(const float *x, const float *gamma, float eps, float *y,
                                 uint8_t *q8, int64_t K, int nt, hipStream_t s);
 hipError_t launch_swiglu_quant(const float *g, const float *u, float *y, uint8_t *q8, int64_t K,
                                int nt, hipStream_t s);
-hipError_t launch_repack(const uint8_t *raw, uint8_t *dpl, int64_t N, int64_t K, hipStream_t s);
-void repack_host(const uint8_t *raw, uint8_t *dpl, int64_t N, int64_t K);
-void unpack_host(const uint8_t *dpl, uint8_t *raw, int64_t N, int64_t K);
+hipError_t launch_repack(int type, const uint8_t *raw, uint8_t *dpl, int64_t N, int64_t K,
+                         hipStream_t s);
+void repack_host(int type, const uint8_t *raw, uint8_t *dpl, int64_t N, int64_t K);
+void unpack_host(int type, const uint8_t *dpl, uint8_t *raw, int64_t N, int64_t K);
 
 }  // namespace q6k

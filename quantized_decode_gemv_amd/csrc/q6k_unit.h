@@ -22,6 +22,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "bufload.h"
+#include "kq_format.h"
+
 namespace q6k {
 
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t bits)
@@ -147,5 +150,54 @@ __device__ __forceinline__ float chunk_accumulate(float acc, const ChunkW &w, co
 {
     return __builtin_fmaf(d, chunk_partial_nod(w, a, Q), acc);
 }
+
+// Byte offsets of one chunk's operands inside a dpl row.
+struct ChunkOffs {
+    uint32_t ql, qh, sc, d;
+};
+
+// Format policy for q6_K dpl rows, the interface the GEMV kernels are written
+// against (offsets, loads, activation operands, the chunk's contribution).
+struct FmtQ6K {
+    static constexpr int TYPE = KQT_Q6_K;
+    using W = ChunkW;
+    using Act = ChunkAct;
+    using Offs = ChunkOffs;
+
+    __device__ static Offs offsets(uint32_t Q, uint32_t nbe)
+    {
+        const uint32_t G = Q >> 2;
+        Offs o;
+        o.ql = 16u * Q;
+        o.qh = 128u * nbe + 16u * (2u * G + (Q & 1u));
+        o.sc = 192u * nbe + 8u * G;
+        o.d = 208u * nbe + 2u * (Q >> 3);
+        return o;
+    }
+
+    // Low/high bits are streamed (non-temporal); the scale group and d keep the
+    // default policy (each 64-byte line of them is touched by three load
+    // instructions of the same row).
+    __device__ static W load(__amdgpu_buffer_rsrc_t r, const Offs &o)
+    {
+        W w;
+        w.ql = load_b128<POLICY_STREAM>(r, o.ql);
+        w.qh = load_b128<POLICY_STREAM>(r, o.qh);
+        w.sc = load_b64<POLICY_DEFAULT>(r, o.sc);
+        w.d = load_b16<POLICY_DEFAULT>(r, o.d);
+        return w;
+    }
+
+    __device__ static Act act(const int8_t *qs_t, const uint16_t *d8_t, uint32_t Q)
+    {
+        return load_act(qs_t, d8_t, Q);
+    }
+
+    __device__ static float accumulate(float acc, const W &w, const Act &a, uint32_t Q, bool live)
+    {
+        const float d = live ? f16_bits_to_f32(w.d) : 0.0f;   // 0 drops the chunk
+        return chunk_accumulate(acc, w, a, Q, d);
+    }
+};
 
 }  // namespace q6k

@@ -205,3 +205,82 @@ def test_fused_rmsnorm_mmvq_shape_rule(nbe, nt):
     assert q.rmsnorm_mmvq_fused(1000, K, nt) == expect
     if expect:
         assert q.mmvq_plan(1000, K, nt, 256)["hoist"]
+
+
+# --- q4_K / q5_K by weight type ------------------------------------------------------
+
+KQ_TYPES = [q.KQ_Q4_K, q.KQ_Q5_K]
+
+
+@pytest.mark.parametrize("qtype", KQ_TYPES)
+@pytest.mark.parametrize("nbe", [1, 4, 20, 54, 97])
+def test_kq_sizes_match_oracle(qtype, nbe):
+    K = 256 * nbe
+    assert q.kq_block_bytes(qtype) == oracle.kq_block_bytes(qtype)
+    assert q.kq_dpl_row_stride(qtype, K) == oracle.kq_row_stride(qtype, oracle.DPL, K)
+    assert q.kq_dpl_bytes(qtype, 7, K) == 7 * oracle.kq_row_stride(qtype, oracle.DPL, K)
+    assert q.kq_raw_bytes(qtype, 7, K) == 7 * oracle.kq_row_stride(qtype, oracle.RAW, K)
+
+
+def test_kq_q6k_type_equals_the_q6k_entries():
+    for K in (256, 5120, 18944):
+        assert q.kq_dpl_row_stride(q.KQ_Q6_K, K) == q.q6k_dpl_row_stride(K)
+        assert q.kq_dpl_bytes(q.KQ_Q6_K, 3, K) == q.q6k_dpl_bytes(3, K)
+        assert q.kq_raw_bytes(q.KQ_Q6_K, 3, K) == q.q6k_raw_bytes(3, K)
+    assert q.kq_block_bytes(q.KQ_Q6_K) == 210
+
+
+@pytest.mark.parametrize("qtype", KQ_TYPES)
+@pytest.mark.parametrize("N,K", [(1, 256), (5, 5120), (3, 13824), (2, 256 * 97)])
+def test_kq_host_repack_matches_oracle_and_round_trips(qtype, N, K):
+    raw = q6ksynth.raw_kq(qtype, N, K, seed=N + K + qtype)
+    dpl = np.full(q.kq_dpl_bytes(qtype, N, K), 0xEE, np.uint8)
+    q.repack_kq_dpl_host(qtype, raw, dpl, N, K)
+    assert np.array_equal(dpl, oracle.kq_repack_dpl(qtype, raw, N, K))
+    back = np.zeros_like(raw)
+    q.unpack_kq_dpl_host(qtype, dpl, back, N, K)
+    assert np.array_equal(back, raw)
+
+
+def test_kq_host_repack_q6k_type_matches_q6k_repack():
+    N, K = 3, 5120
+    raw = q6ksynth.raw_q6k(N, K, seed=9)
+    a = np.zeros(q.q6k_dpl_bytes(N, K), np.uint8)
+    b = np.zeros_like(a)
+    q.repack_q6k_dpl_host(raw, a, N, K)
+    q.repack_kq_dpl_host(q.KQ_Q6_K, raw, b, N, K)
+    assert np.array_equal(a, b)
+
+
+E_TYPE = -6
+
+
+@pytest.mark.parametrize("bad", [0, 11, 15, -1, 2])
+def test_kq_rejects_unknown_types(bad):
+    assert q.kq_block_bytes(bad) == 0 and q.kq_dpl_row_stride(bad, 256) == 0
+    assert q.kq_dpl_bytes(bad, 1, 256) == 0 and q.kq_raw_bytes(bad, 1, 256) == 0
+    assert _code(q.mmvq_kq_q8, bad, A, B, C, 4, 256, 1, 0) == E_TYPE
+    assert _code(q.repack_kq_dpl, bad, A, B, 1, 256, 0) == E_TYPE
+    assert _code(q.mmvq_kq_q8_subdots, bad, A, B, C, 4, 256, 1, 0) == E_TYPE
+    assert _code(q.mmvq_kq_rmsnorm_q8, bad, A, B, C, 1e-6, None, D, 0x50000000, 4, 256, 1,
+                 0) == E_TYPE
+    buf = np.zeros(4096, np.uint8)
+    assert _code(q.repack_kq_dpl_host, bad, buf[:2048], buf[2048:], 1, 256) == E_TYPE
+    assert _code(q.unpack_kq_dpl_host, bad, buf[:2048], buf[2048:], 1, 256) == E_TYPE
+
+
+@pytest.mark.parametrize("qtype", KQ_TYPES)
+def test_kq_gemv_rejects_bad_arguments(qtype):
+    f = q.mmvq_kq_q8
+    assert _code(f, qtype, A, B, C, 4, 288, 1, 0) == E_SHAPE
+    assert _code(f, qtype, A, B, C, 0, 256, 1, 0) == E_SHAPE
+    assert _code(f, qtype, None, B, C, 4, 256, 1, 0) == E_NULL
+    assert _code(f, qtype, A + 8, B, C, 4, 256, 1, 0) == E_ALIGN
+    assert _code(f, qtype, A, B, A + 16, 4, 256, 1, 0) == E_ALIAS
+    # the weight extent is the type's: a y just past a q4_K matrix is fine for the
+    # length check of q4_K but inside the bigger q5_K one
+    n = q.kq_dpl_bytes(q.KQ_Q4_K, 4, 256)
+    if qtype == q.KQ_Q5_K:
+        assert _code(f, qtype, A, B, A + n, 4, 256, 1, 0) == E_ALIAS
+    assert _code(q.mmvq_kq_q8_subdots, qtype, A, B, B, 4, 256, 1, 0) == E_ALIAS
+    assert _code(q.repack_kq_dpl, qtype, A, A + 64, 1, 256, 0) == E_ALIAS
