@@ -225,8 +225,7 @@ int mmvq_kq_rmsnorm_q8(int type, const void *w_dpl, const float *x, const float 
 int mmvq_kq_q8_subdots(int type, const void *w_dpl, const void *q8, int32_t *dots, int64_t N,
                        int64_t K, int nt, void *stream);
 
-/* Diagnostics: how mmvq_q6k_q8 (and mmvq_kq_q8, the same for every type) runs a
- * shape on a device with num_cu compute units.
+/* Diagnostics: how mmvq_q6k_q8 runs a shape on a device with num_cu compute units.
  * out6[0] = workgroups per launch (256 threads each; a launch uses fewer where the
  * kernel's registers fit fewer workgroups per CU), out6[1] = low-bit chunks per
  * lane per row, out6[2] = 1 for a fixed-length kernel (0: the generic stepping
@@ -234,6 +233,10 @@ int mmvq_kq_q8_subdots(int type, const void *w_dpl, const void *q8, int32_t *dot
  * out6[4] = launches (one per group of up to 4 token columns), out6[5] = rows in
  * flight per wave. Host only. */
 int q6k_mmvq_plan(int64_t N, int64_t K, int nt, int num_cu, int32_t *out6);
+
+/* The same for mmvq_kq_q8 with weight type `type` (Q6K_E_TYPE for an unknown one);
+ * the shape choices depend on the type. */
+int kq_mmvq_plan(int type, int64_t N, int64_t K, int nt, int num_cu, int32_t *out6);
 
 #ifdef __cplusplus
 }

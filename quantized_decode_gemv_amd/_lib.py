@@ -51,6 +51,7 @@ _SIGS = {
                                   _INT, _P]),
     "mmvq_kq_q8_subdots": (_INT, [_INT, _P, _P, _P, _I64, _I64, _INT, _P]),
     "q6k_mmvq_plan": (_INT, [_I64, _I64, _INT, _INT, _P]),
+    "kq_mmvq_plan": (_INT, [_INT, _I64, _I64, _INT, _INT, _P]),
 }
 
 _lock = threading.Lock()
@@ -223,9 +224,9 @@ def mmvq_q6k_q8_subdots(w_dpl, q8, dots, N: int, K: int, nt: int, stream=None) -
           _stream(stream))
 
 
-def mmvq_plan(N: int, K: int, nt: int, num_cu: int) -> dict:
+def mmvq_plan(N: int, K: int, nt: int, num_cu: int, qtype: int = 14) -> dict:
     out = (ctypes.c_int32 * 6)()
-    _call("q6k_mmvq_plan", N, K, nt, num_cu, ctypes.addressof(out))
+    _call("kq_mmvq_plan", qtype, N, K, nt, num_cu, ctypes.addressof(out))
     return dict(grid=out[0], cpl=out[1], unrolled=bool(out[2]), hoist=bool(out[3]),
                 launches=out[4], depth=out[5])
 

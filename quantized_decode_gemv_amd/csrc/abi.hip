@@ -332,13 +332,15 @@ int mmvq_q6k_q8_subdots(const void *w_dpl, const void *q8, int32_t *dots, int64_
     return mmvq_kq_q8_subdots(KQ_Q6_K, w_dpl, q8, dots, N, K, nt, stream);
 }
 
-int q6k_mmvq_plan(int64_t N, int64_t K, int nt, int num_cu, int32_t *out6)
+int kq_mmvq_plan(int type, int64_t N, int64_t K, int nt, int num_cu, int32_t *out6)
 {
+    if (!q6k::kq_known(type))
+        return Q6K_E_TYPE;
     if (!weight_shape_ok(N, K) || !act_shape_ok(K, nt) || num_cu < 1)
         return Q6K_E_SHAPE;
     if (!out6)
         return Q6K_E_NULL;
-    const q6k::MmvqPlan p = q6k::plan_mmvq(N, K, nt, num_cu);
+    const q6k::MmvqPlan p = q6k::plan_mmvq(type, N, K, nt, num_cu);
     out6[0] = (int32_t)p.grid;
     out6[1] = p.cpl;
     out6[2] = p.unrolled;
@@ -346,6 +348,11 @@ int q6k_mmvq_plan(int64_t N, int64_t K, int nt, int num_cu, int32_t *out6)
     out6[4] = p.launches;
     out6[5] = p.depth;
     return Q6K_OK;
+}
+
+int q6k_mmvq_plan(int64_t N, int64_t K, int nt, int num_cu, int32_t *out6)
+{
+    return kq_mmvq_plan(KQ_Q6_K, N, K, nt, num_cu, out6);
 }
 
 }  // extern "C"

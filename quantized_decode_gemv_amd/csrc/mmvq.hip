@@ -581,21 +581,48 @@ __global__ __launch_bounds__(WG) void mmvq_subdots_kernel(const uint8_t *__restr
 
 namespace {
 
-// The fixed-length kernel's shape for (NT, CPL): rows in flight per wave, whether the
-// activation operands stay in registers, and workgroups per CU, chosen so that
-// weights-in-flight plus activation registers stay near 150 VGPRs.
+// The fixed-length kernel's shape: rows in flight per wave, whether the activation
+// operands stay in registers, and workgroups per CU (a launch takes fewer if the
+// kernel's registers fit fewer). Chosen per weight type, tokens per launch and chunks
+// per lane from measurements on MI355X (sweeps at about 100 MB per matrix and on
+// the workload shapes; choices within about 2 % of each other are merged):
+//  - short rows (1-2 chunks per lane) need many rows in flight per CU: more
+//    workgroups and depth 2-3;
+//  - q4_K / q5_K rows carry more ALU work per byte than q6_K rows and gain from two
+//    waves per SIMD where q6_K keeps one wave at depth 3 (1-3 chunks);
+//  - middle rows (4-7 chunks) take depth 2 with the activation in registers;
+//  - long rows (8-12 chunks, and 7 for q5_K) take depth 1, activations re-read.
+// Several tokens multiply the activation registers; past 4 chunks they take the
+// register-budget rule: depth 2 in registers while nt * chunks <= 6, else depth 1.
 struct RowsCfg {
     int depth;
     bool hoist;
     int wg_per_cu;
 };
 
-RowsCfg rows_cfg(int nt, int cpl)
+constexpr RowsCfg rows_cfg(int type, int nt, int cpl)
 {
-    const int work = nt * cpl;
-    if (work <= 3)
-        return {3, true, 1};
-    if (work <= 6 || (cpl <= 3 && work <= 12))
+    const bool q6 = type == KQT_Q6_K;
+    if (nt == 1) {
+        if (cpl == 1)
+            return {2, true, 4};
+        if (cpl == 2)
+            return q6 ? RowsCfg{2, true, 2} : RowsCfg{3, true, 2};
+        if (cpl == 3)
+            return q6 ? RowsCfg{3, true, 1} : RowsCfg{2, true, 2};
+        if (cpl <= 6 || (cpl == 7 && type != KQT_Q5_K))
+            return {2, true, 1};
+        return {1, false, 2};
+    }
+    if (cpl == 1)
+        return {3, true, 2};
+    if (cpl == 2)
+        return (nt == 2 && !q6) ? RowsCfg{3, true, 2} : RowsCfg{2, true, 2};
+    if (cpl == 3)
+        return {2, true, 2};
+    if (cpl == 4)
+        return (nt == 2 && q6) ? RowsCfg{2, true, 1} : RowsCfg{2, true, 2};
+    if (nt * cpl <= 6)
         return {2, true, 2};
     return {1, false, 2};
 }
@@ -651,18 +678,11 @@ hipError_t launch(Kern kern, int num_cu, int wg_per_cu, hipStream_t s, GemvArgs 
 template <class F, int NT, int CPL>
 hipError_t launch_cpl(const RowsCfg &c, int num_cu, hipStream_t s, const GemvArgs &a)
 {
-    // only the (depth, hoist) pairs rows_cfg can pick for this NT * CPL are built
-    if constexpr (NT * CPL <= 3) {
-        if (c.depth == 3)
-            return launch(mmvq_rows<F, NT, CPL, 3, true>, num_cu, c.wg_per_cu, s, a);
-    } else if constexpr (NT * CPL <= 6 || (CPL <= 3 && NT * CPL <= 12)) {
-        if (c.depth == 2)
-            return launch(mmvq_rows<F, NT, CPL, 2, true>, num_cu, c.wg_per_cu, s, a);
-    } else {
-        if (c.depth == 1)
-            return launch(mmvq_rows<F, NT, CPL, 1, false>, num_cu, c.wg_per_cu, s, a);
-    }
-    return hipErrorInvalidValue;
+    // the one (depth, hoist) pair rows_cfg picks for this type, NT and CPL is built
+    constexpr RowsCfg k = rows_cfg(F::TYPE, NT, CPL);
+    if (c.depth != k.depth || c.hoist != k.hoist)
+        return hipErrorInvalidValue;
+    return launch(mmvq_rows<F, NT, CPL, k.depth, k.hoist>, num_cu, c.wg_per_cu, s, a);
 }
 
 template <class F, int NT, int... CPLS>
@@ -706,15 +726,11 @@ hipError_t launch_fused_cpl(int depth, int num_cu, int wg_per_cu, hipStream_t s,
                         (void *)&a.xn, (void *)&a.qs, (void *)&a.d8, (void *)&a.y,
                         (void *)&a.N, (void *)&a.nbe, (void *)&a.stride, (void *)&a.K,
                         (void *)&a.ldy};
-        // the (depth, hoist) pair rows_cfg picks for this NT * CPL
-        const void *kern = nullptr;
-        if constexpr (NT * CPL <= 3) {
-            if (depth == 3)
-                kern = (const void *)mmvq_rmsnorm_rows<F, NT, CPL, 3>;
-        } else {
-            if (depth == 2)
-                kern = (const void *)mmvq_rmsnorm_rows<F, NT, CPL, 2>;
-        }
+        // the depth rows_cfg picks for this type, NT and CPL (always in registers here)
+        constexpr RowsCfg k = rows_cfg(F::TYPE, NT, CPL);
+        static_assert(k.hoist, "the fused kernel keeps the activation in registers");
+        const void *kern = depth == k.depth ? (const void *)mmvq_rmsnorm_rows<F, NT, CPL, k.depth>
+                                            : nullptr;
         const int fit = kern ? wg_fit(kern) : 0;
         if (fit >= 1) {
             const uint32_t g = grid_for(a.N, num_cu, wg_per_cu < fit ? wg_per_cu : fit);
@@ -758,7 +774,7 @@ hipError_t launch_mmvq_fmt(const uint8_t *w, const uint8_t *q8, float *y, int64_
         a.ldy = (uint32_t)N;
         hipError_t e;
         if (cpl <= MAX_CPL) {
-            const RowsCfg c = rows_cfg(n, cpl);
+            const RowsCfg c = rows_cfg(F::TYPE, n, cpl);
             const auto seq = std::make_integer_sequence<int, MAX_CPL>{};
             switch (n) {
             case 1: e = dispatch_cpl<F, 1>(cpl, c, seq, num_cu, s, a); break;
@@ -787,7 +803,7 @@ hipError_t launch_fused_fmt(const uint8_t *w, const float *x, const float *gamma
 {
     const uint32_t nbe = (uint32_t)(K / 256);
     const int cpl = (int)((8u * nbe + 63u) / 64u);
-    const RowsCfg c = rows_cfg(1, cpl);
+    const RowsCfg c = rows_cfg(F::TYPE, 1, cpl);
     FusedArgs a;
     a.w = w;
     a.x = reinterpret_cast<const float4 *>(x);
@@ -808,7 +824,7 @@ hipError_t launch_fused_fmt(const uint8_t *w, const float *x, const float *gamma
 
 }  // namespace
 
-MmvqPlan plan_mmvq(int64_t N, int64_t K, int nt, int num_cu)
+MmvqPlan plan_mmvq(int type, int64_t N, int64_t K, int nt, int num_cu)
 {
     MmvqPlan p;
     const int64_t nbe = K / 256;
@@ -816,7 +832,7 @@ MmvqPlan plan_mmvq(int64_t N, int64_t K, int nt, int num_cu)
     p.unrolled = p.cpl <= MAX_CPL;
     p.launches = (nt + MAX_NT_KERNEL - 1) / MAX_NT_KERNEL;
     const int nt0 = nt < MAX_NT_KERNEL ? nt : MAX_NT_KERNEL;
-    const RowsCfg c = p.unrolled ? rows_cfg(nt0, p.cpl) : RowsCfg{1, false, 2};
+    const RowsCfg c = p.unrolled ? rows_cfg(type, nt0, p.cpl) : RowsCfg{1, false, 2};
     p.hoist = p.unrolled && c.hoist;
     p.depth = c.depth;
     p.grid = grid_for(N, num_cu, c.wg_per_cu);

@@ -11,7 +11,7 @@ namespace q6k {
 
 // How mmvq_q6k_q8 will run a shape (for tests and reports).
 struct MmvqPlan {
-    uint32_t grid = 0;      // workgroups of 256 threads
+    uint32_t grid = 0;      // workgroups of 256 threads (before the occupancy clamp)
     int cpl = 0;            // low-bit chunks per lane per row
     bool unrolled = false;  // a fixed-CPL kernel (else the generic stepping kernel)
     bool hoist = false;     // activation operands held in registers across rows
@@ -19,7 +19,7 @@ struct MmvqPlan {
     int depth = 1;          // rows in flight per wave
 };
 
-MmvqPlan plan_mmvq(int64_t N, int64_t K, int nt, int num_cu);
+MmvqPlan plan_mmvq(int type, int64_t N, int64_t K, int nt, int num_cu);
 
 // type: a KqType of kq_format.h (the weight rows are that type's split-plane rows).
 hipError_t launch_mmvq(int type, const uint8_t *w, const uint8_t *q8, float *y, int64_t N,
