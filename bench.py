@@ -135,9 +135,12 @@ def main() -> int:
     ap.add_argument("--workload", default="lm_head")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
-    ap.add_argument("--path", choices=["fused", "split"], default="fused",
+    ap.add_argument("--path", choices=["fused", "split", "formb"], default="fused",
                     help="fused: one RMSNorm -> q8 -> GEMV call per step (RMSNorm workloads "
-                         "only); split: the producer kernel, then the GEMV kernel")
+                         "only); split: the producer kernel, then the GEMV kernel; formb: "
+                         "gate+up GEMV, SwiGLU and q8 in one call on a resident q8 row "
+                         "(gate+up workloads, one token), against the GEMV then the SwiGLU "
+                         "producer")
     ap.add_argument("--graph", type=int, default=0, metavar="G",
                     help="run the timed steps as replays of a HIP graph holding G steps")
     args = ap.parse_args()
@@ -211,7 +214,32 @@ def main() -> int:
         produce(st)
         gemv(i, st)
 
-    step = fused_call if fused else split_step
+    formb = args.path == "formb"
+    if formb:
+        # the matrix is [gate rows; up rows]; the activation row's q8 plane stays resident
+        if nt != 1 or N % 64:
+            print("--path formb takes one token and an even number of 32-row blocks",
+                  file=sys.stderr)
+            return 2
+        Nh = N // 2
+        produce(stream)
+        torch.cuda.synchronize()
+        gu = torch.empty(N, dtype=torch.float32, device=dev)
+        y_sw = torch.empty(Nh, dtype=torch.float32, device=dev)
+        plane_out = torch.empty(q.q8_plane_bytes(Nh, 1), dtype=torch.uint8, device=dev)
+
+        def formb_call(i, st):
+            q.mmvq_kq_gate_up_swiglu_q8(qt, Ws[i % copies], plane, gu, None, plane_out, Nh, K,
+                                        1, st)
+
+        def gemv_swiglu(i, st):
+            q.mmvq_kq_q8(qt, Ws[i % copies], plane, gu, N, K, 1, st)
+            q.swiglu_quant_q8(gu[:Nh], gu[Nh:], y_sw, plane_out, Nh, 1, st)
+
+        fused = False
+        step, split_step = formb_call, gemv_swiglu
+    else:
+        step = fused_call if fused else split_step
 
     def time_steps(fn, n):
         t0 = time.perf_counter()
@@ -234,7 +262,7 @@ def main() -> int:
 
     for i in range(args.warmup):
         step(i, stream)
-        if fused:
+        if fused or formb:
             split_step(i, stream)
     torch.cuda.synchronize()
 
@@ -262,11 +290,16 @@ def main() -> int:
         ms_per_step = (time.perf_counter() - t0) * 1e3 / (reps * G)
     else:
         ms_per_step = time_steps(step, args.steps)
-    ms_per_step_split = time_steps(split_step, args.steps) if fused else None
+    ms_per_step_split = time_steps(split_step, args.steps) if (fused or formb) else None
 
-    # The dominant kernel alone: the fused kernel (fused path) or the GEMV kernel.
-    kern_us = time_back_to_back(fused_call if fused else gemv, args.steps)
-    gemv_us = time_back_to_back(gemv, args.steps) if fused else kern_us
+    # The dominant kernel alone: the fused kernel (fused path, Form B) or the GEMV kernel.
+    if formb:
+        kern_us = time_back_to_back(formb_call, args.steps)
+        gemv_us = time_back_to_back(lambda i, st: q.mmvq_kq_q8(qt, Ws[i % copies], plane, gu, N, K,
+                                                               1, st), args.steps)
+    else:
+        kern_us = time_back_to_back(fused_call if fused else gemv, args.steps)
+        gemv_us = time_back_to_back(gemv, args.steps) if fused else kern_us
 
     # Diagnostic: events around every GEMV inside producer+GEMV steps (these also
     # count each launch's dispatch latency).
@@ -285,7 +318,8 @@ def main() -> int:
     content = w.content_bytes
     value = content / (ms_per_step * 1e-3) / 1e9
     achieved = content / (kern_us * 1e-6) / 1e9
-    traffic = recorded_traffic(f"{'fused' if fused else 'gemv'}_nt{nt}")
+    traffic = (None if formb or w.name != "lm_head"
+               else recorded_traffic(f"{'fused' if fused else 'gemv'}_nt{nt}"))
     plan = q.mmvq_plan(N, K, nt, torch.cuda.get_device_properties(0).multi_processor_count)
 
     out = {
@@ -304,14 +338,17 @@ def main() -> int:
         "config": {"workload": f"{w.name} {TYPE_NAMES[qt]} GEMV N={N} K={K} nt={nt}: "
                                + (f"RMSNorm->q8->split-plane {TYPE_NAMES[qt]} x q8 MMVQ in one "
                                   f"kernel" if fused else
+                                  f"Form B: gate+up {TYPE_NAMES[qt]} GEMV, SwiGLU and q8 in one "
+                                  f"kernel on a resident q8 row" if formb else
                                   f"{PRODUCER_NAMES[w.producer]} producer + split-plane "
                                   f"{TYPE_NAMES[qt]} x q8 MMVQ"),
                    "N": N, "K": K, "nt": nt, "content_bytes": content,
                    "dpl_bytes": dpl_bytes, "weight_copies": copies},
-        "dominant_kernel": "mmvq_rmsnorm_rows (fused)" if fused else "mmvq_rows",
+        "dominant_kernel": ("mmvq_rmsnorm_rows (fused)" if fused else
+                            "gate_up_swiglu_rows (Form B)" if formb else "mmvq_rows"),
         "us_per_dominant_kernel": round(kern_us, 2),
         "us_per_gemv": round(gemv_us, 2),
-        "ms_per_step_split": round(ms_per_step_split, 5) if fused else None,
+        "ms_per_step_split": round(ms_per_step_split, 5) if ms_per_step_split else None,
         "us_per_gemv_inline_events": {"mean": round(kern_inline_us, 2),
                                       "median": round(kern_inline_med_us, 2)},
         "pct_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),

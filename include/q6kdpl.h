@@ -219,6 +219,25 @@ int mmvq_kq_rmsnorm_q8(int type, const void *w_dpl, const float *x, const float 
                        float eps, float *xn, void *q8, float *y, int64_t N, int64_t K, int nt,
                        void *stream);
 
+/* Form B: gate+up GEMV, SwiGLU and q8 of one token ([D4-4] §3.5, the archived fused
+ * gate+up+SwiGLU+q8 shape, and §5, its closing numbers; [D3-5] §3.2, the SwiGLU
+ * producer's body). w_gu holds 2*Nh split-plane rows of `type`: the Nh gate rows,
+ * then the Nh up rows. With x the q8 activation row q8_in (K activations):
+ *   gu = W x (float32 [2*Nh], as mmvq_kq_q8 writes it),
+ *   y = (g / (1 + e^-g)) * u for g = gu[0:Nh], u = gu[Nh:2Nh] (float32 [Nh], written
+ *       when y is not NULL), and q8_out = its q8 plane (q8_plane_bytes(Nh, 1) bytes),
+ * bit for bit as mmvq_kq_q8 followed by swiglu_quant_q8. Where
+ * kq_gate_up_swiglu_fused(Nh, K) is 1 (K <= 12288) this is one kernel, each
+ * workgroup taking the 64 rows behind whole 32-output q8 blocks; otherwise the two
+ * kernels are queued. nt must be 1 and Nh a multiple of 32 (Q6K_E_SHAPE otherwise).
+ * All device, 16-B aligned; no output may overlap an input or another output. */
+int mmvq_kq_gate_up_swiglu_q8(int type, const void *w_gu, const void *q8_in, float *gu, float *y,
+                              void *q8_out, int64_t Nh, int64_t K, int nt, void *stream);
+
+/* Diagnostics: 1 when mmvq_kq_gate_up_swiglu_q8 runs (Nh, K) as one kernel, 0 when it
+ * queues the GEMV and the SwiGLU producer, Q6K_E_SHAPE on a bad shape. Host only. */
+int kq_gate_up_swiglu_fused(int64_t Nh, int64_t K);
+
 /* Test entry: the exact integer dots of mmvq_kq_q8. KQ_Q6_K: as mmvq_q6k_q8_subdots
  * (K/16 per row). KQ_Q4_K / KQ_Q5_K: Dq per 32-element sub-block,
  * dots[(t*N + r)*(K/32) + s] (int32, device, 16-B aligned). */

@@ -50,6 +50,8 @@ _SIGS = {
     "mmvq_kq_rmsnorm_q8": (_INT, [_INT, _P, _P, _P, ctypes.c_float, _P, _P, _P, _I64, _I64,
                                   _INT, _P]),
     "mmvq_kq_q8_subdots": (_INT, [_INT, _P, _P, _P, _I64, _I64, _INT, _P]),
+    "mmvq_kq_gate_up_swiglu_q8": (_INT, [_INT, _P, _P, _P, _P, _P, _I64, _I64, _INT, _P]),
+    "kq_gate_up_swiglu_fused": (_INT, [_I64, _I64]),
     "q6k_mmvq_plan": (_INT, [_I64, _I64, _INT, _INT, _P]),
     "kq_mmvq_plan": (_INT, [_INT, _I64, _I64, _INT, _INT, _P]),
 }
@@ -295,3 +297,22 @@ def mmvq_kq_q8_subdots(qtype: int, w_dpl, q8, dots, N: int, K: int, nt: int,
     _need("dots", dots, 4 * max(N, 0) * max(nt, 0) * max(per_row, 0))
     _call("mmvq_kq_q8_subdots", qtype, _addr(w_dpl), _addr(q8), _addr(dots), N, K, nt,
           _stream(stream))
+
+
+def mmvq_kq_gate_up_swiglu_q8(qtype: int, w_gu, q8_in, gu, y, q8_out, Nh: int, K: int,
+                              nt: int = 1, stream=None) -> None:
+    _need("w_gu", w_gu, kq_dpl_bytes(qtype, 2 * Nh, K))
+    _need("q8_in", q8_in, q8_plane_bytes(K, 1))
+    _need("gu", gu, 8 * max(Nh, 0))
+    if y is not None:
+        _need("y", y, 4 * max(Nh, 0))
+    _need("q8_out", q8_out, q8_plane_bytes(Nh, 1))
+    _call("mmvq_kq_gate_up_swiglu_q8", qtype, _addr(w_gu), _addr(q8_in), _addr(gu), _addr(y),
+          _addr(q8_out), Nh, K, nt, _stream(stream))
+
+
+def gate_up_swiglu_fused(Nh: int, K: int) -> bool:
+    rc = lib().kq_gate_up_swiglu_fused(Nh, K)
+    if rc < 0:
+        raise Q6kError("kq_gate_up_swiglu_fused", rc)
+    return bool(rc)

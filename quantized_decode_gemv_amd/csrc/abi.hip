@@ -303,6 +303,49 @@ int q6k_rmsnorm_mmvq_fused(int64_t N, int64_t K, int nt)
     return q6k::rmsnorm_mmvq_fused(K, nt) ? 1 : 0;
 }
 
+int mmvq_kq_gate_up_swiglu_q8(int type, const void *w_gu, const void *q8_in, float *gu, float *y,
+                              void *q8_out, int64_t Nh, int64_t K, int nt, void *stream)
+{
+    if (!q6k::kq_known(type))
+        return Q6K_E_TYPE;
+    if (nt != 1 || Nh < 1 || Nh % 32 || Nh > Q6K_MAX_K || !weight_shape_ok(2 * Nh, K) ||
+        !act_shape_ok(K, 1))
+        return Q6K_E_SHAPE;
+    if (!w_gu || !q8_in || !gu || !q8_out)
+        return Q6K_E_NULL;
+    if (!aligned16(w_gu) || !aligned16(q8_in) || !aligned16(gu) || !aligned16(q8_out) ||
+        (y && !aligned16(y)))
+        return Q6K_E_ALIGN;
+    const size_t nw = kq_dpl_bytes(type, 2 * Nh, K), nq = q8_plane_bytes(K, 1);
+    const size_t ngu = (size_t)2 * Nh * 4u, ny = (size_t)Nh * 4u, nqo = q8_plane_bytes(Nh, 1);
+    const void *in[2] = {w_gu, q8_in};
+    const size_t in_n[2] = {nw, nq};
+    const void *out[3] = {gu, q8_out, y};
+    const size_t out_n[3] = {ngu, nqo, y ? ny : 0};
+    for (int o = 0; o < 3; ++o) {
+        for (int i = 0; i < 2; ++i)
+            if (overlap(out[o], out_n[o], in[i], in_n[i]))
+                return Q6K_E_ALIAS;
+        for (int p = o + 1; p < 3; ++p)
+            if (overlap(out[o], out_n[o], out[p], out_n[p]))
+                return Q6K_E_ALIAS;
+    }
+    int cu = 0;
+    int rc = cu_count((hipStream_t)stream, &cu);
+    if (rc != Q6K_OK)
+        return rc;
+    return from_hip(q6k::launch_gate_up_swiglu(type, (const uint8_t *)w_gu, (const uint8_t *)q8_in,
+                                               gu, y, (uint8_t *)q8_out, Nh, K, cu,
+                                               (hipStream_t)stream));
+}
+
+int kq_gate_up_swiglu_fused(int64_t Nh, int64_t K)
+{
+    if (Nh < 1 || Nh % 32 || Nh > Q6K_MAX_K || !weight_shape_ok(2 * Nh, K))
+        return Q6K_E_SHAPE;
+    return q6k::gate_up_swiglu_fused(K) ? 1 : 0;
+}
+
 int mmvq_kq_q8_subdots(int type, const void *w_dpl, const void *q8, int32_t *dots, int64_t N,
                        int64_t K, int nt, void *stream)
 {

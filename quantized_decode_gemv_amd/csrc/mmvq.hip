@@ -193,11 +193,13 @@ __device__ __forceinline__ void load_row(typename F::W (&dst)[CPL], const uint8_
         dst[i] = F::load(r, st.off[i]);
 }
 
+// The row's totals for its token columns: lane l holds the total of token
+// (l & 3) (NT = 2: l & 1; NT = 1: every lane the only token's).
 template <class F, int NT, int CPL, bool HOIST>
-__device__ __forceinline__ void finish_row(const typename F::W (&src)[CPL],
+__device__ __forceinline__ float row_total(const typename F::W (&src)[CPL],
                                            const LaneState<F, NT, CPL, HOIST> &st,
                                            const int8_t *qs, const uint16_t *d8, uint32_t K,
-                                           float *y, uint32_t ldy, uint32_t row, uint32_t lane)
+                                           uint32_t lane)
 {
     float acc[NT];
 #pragma unroll
@@ -216,7 +218,16 @@ __device__ __forceinline__ void finish_row(const typename F::W (&src)[CPL],
             }
         }
     }
-    const float s = reduce_tokens<NT>(acc, lane);
+    return reduce_tokens<NT>(acc, lane);
+}
+
+template <class F, int NT, int CPL, bool HOIST>
+__device__ __forceinline__ void finish_row(const typename F::W (&src)[CPL],
+                                           const LaneState<F, NT, CPL, HOIST> &st,
+                                           const int8_t *qs, const uint16_t *d8, uint32_t K,
+                                           float *y, uint32_t ldy, uint32_t row, uint32_t lane)
+{
+    const float s = row_total<F, NT, CPL, HOIST>(src, st, qs, d8, K, lane);
     uint32_t t;
     if (stores_token<NT>(lane, t))
         y[(size_t)t * ldy + row] = s;
@@ -457,6 +468,82 @@ __global__ __launch_bounds__(WG) void mmvq_rmsnorm_rows(
     __builtin_amdgcn_sched_barrier(0);
     stream_rows_primed<F, NT, CPL, DEPTH, true>(A, B, Cb, w, wave, nw, N, stride, st, nullptr,
                                                 nullptr, K, y, ldy, lane);
+}
+
+// Form B (D4-4 §3.5, the archived fused gate+up+SwiGLU+q8 shape; §5 its closing
+// numbers): the gate+up GEMV of one token, then y = silu(gate) * up and its q8 plane,
+// in one kernel. The matrix holds the Nh gate rows, then the Nh up rows. Output block
+// b (32 activations, one q8 block) needs gate rows 32b .. 32b+31 and up rows Nh + 32b
+// .. Nh + 32b + 31: a workgroup takes whole blocks (wave v: gate and up rows 32b + 8v
+// .. +7, 16 rows, DEPTH 2 in flight), stores the 64 row totals to gu and LDS, and wave
+// 0 then forms the block's 32 outputs and quantizes them. Row totals, SwiGLU and the
+// q8 body are the GEMV's and the SwiGLU producer's own code (row_total; the
+// producer's expression; q6k_norm.h), so gu, y and the q8 plane equal mmvq_kq_q8
+// followed by swiglu_quant_q8 bit for bit. The cost against those two kernels is
+// granularity: a q8 block's 64 rows must sit in one workgroup, so Nh / 32 blocks
+// spread over the CUs unevenly (13824 / 32 = 432 blocks on 256 CUs).
+template <class F, int CPL>
+__global__ __launch_bounds__(WG) void gate_up_swiglu_rows(
+    const uint8_t *__restrict__ w, const int8_t *__restrict__ qs, const uint16_t *__restrict__ d8,
+    float *__restrict__ gu, float *__restrict__ y, uint8_t *__restrict__ qs_out,
+    uint16_t *__restrict__ d8_out, uint32_t Nh, uint32_t nbe, uint32_t stride, uint32_t K)
+{
+    constexpr uint32_t ROWS = 16;   // per wave and block: 8 gate rows, then 8 up rows
+    __shared__ float s_g[32], s_u[32];
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    LaneState<F, 1, CPL, true> st;
+    lane_init(st, lane, nbe, qs, d8, K);
+    const uint32_t N = 2u * Nh, nblk = Nh / 32u;
+    typename F::W A[CPL], B[CPL];
+    for (uint32_t b = blockIdx.x; b < nblk; b += gridDim.x) {
+        const uint32_t base = 32u * b + 8u * wv;
+        auto row_of = [&](uint32_t i) { return (i < 8u ? 0u : Nh) + base + (i & 7u); };
+        auto take = [&](uint32_t i, float v) {
+            if (lane == 0) {
+                gu[row_of(i)] = v;
+                (i < 8u ? s_g : s_u)[8u * wv + (i & 7u)] = v;
+            }
+        };
+        load_row(A, w, row_of(0), N, stride, st);
+#pragma unroll
+        for (uint32_t i = 0; i < ROWS; i += 2) {
+            load_row(B, w, row_of(i + 1), N, stride, st);
+            __builtin_amdgcn_sched_barrier(0);
+            take(i, row_total<F, 1, CPL, true>(A, st, nullptr, nullptr, K, lane));
+            if (i + 2 < ROWS) {
+                load_row(A, w, row_of(i + 2), N, stride, st);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            take(i + 1, row_total<F, 1, CPL, true>(B, st, nullptr, nullptr, K, lane));
+        }
+        __syncthreads();
+        if (wv == 0) {
+            // lanes 0..31: the block's outputs; lanes 32..63 carry 0 through the max
+            float v = 0.0f;
+            if (lane < 32u) {
+                const float g = s_g[lane], u = s_u[lane];
+                v = (g / (1.0f + expf(-g))) * u;
+            }
+            float m = fabsf(v);
+            m = fmaxf(m, __shfl_xor(m, 32));
+            m = fmaxf(m, __shfl_xor(m, 16));
+            m = fmaxf(m, __shfl_xor(m, 8));
+            m = fmaxf(m, __shfl_xor(m, 4));
+            m = fmaxf(m, __shfl_xor(m, 2));
+            m = fmaxf(m, __shfl_xor(m, 1));
+            const float d = m / 127.0f;
+            const float di = (d != 0.0f) ? 1.0f / d : 0.0f;
+            if (lane < 32u) {
+                qs_out[32u * b + lane] = (uint8_t)q8_code(v, di);
+                if (y)
+                    y[32u * b + lane] = v;
+            }
+            if (lane == 0)
+                d8_out[b] = __builtin_bit_cast(uint16_t, (_Float16)d);
+        }
+        __syncthreads();   // s_g, s_u are rewritten by the next block
+    }
 }
 
 // Any row length: a row is walked in steps of STEP chunks per lane.
@@ -822,6 +909,55 @@ hipError_t launch_fused_fmt(const uint8_t *w, const float *x, const float *gamma
                                 c.wg_per_cu, s, a);
 }
 
+template <class F, int CPL>
+hipError_t launch_gate_up_cpl(int num_cu, hipStream_t s, const uint8_t *w, const int8_t *qs,
+                              const uint16_t *d8, float *gu, float *y, uint8_t *qs_out,
+                              uint16_t *d8_out, uint32_t Nh, uint32_t nbe, uint32_t stride,
+                              uint32_t K)
+{
+    const void *kern = (const void *)gate_up_swiglu_rows<F, CPL>;
+    const int fit = wg_fit(kern);
+    if (fit < 1)
+        return hipErrorInvalidValue;
+    const uint32_t nblk = Nh / 32u;
+    const uint32_t slots = (uint32_t)num_cu * (uint32_t)(fit < 2 ? fit : 2);
+    const uint32_t grid = nblk < slots ? nblk : slots;
+    void *args[] = {(void *)&w, (void *)&qs, (void *)&d8, (void *)&gu, (void *)&y,
+                    (void *)&qs_out, (void *)&d8_out, (void *)&Nh, (void *)&nbe,
+                    (void *)&stride, (void *)&K};
+    return hipLaunchKernel(kern, dim3(grid), dim3(WG), args, 0, s);
+}
+
+template <class F, int... CPLS>
+hipError_t dispatch_gate_up(int cpl, std::integer_sequence<int, CPLS...>, int num_cu,
+                            hipStream_t s, const uint8_t *w, const int8_t *qs, const uint16_t *d8,
+                            float *gu, float *y, uint8_t *qs_out, uint16_t *d8_out, uint32_t Nh,
+                            uint32_t nbe, uint32_t stride, uint32_t K)
+{
+    hipError_t e = hipErrorInvalidValue;
+    (void)((cpl == CPLS + 1 ? (e = launch_gate_up_cpl<F, CPLS + 1>(num_cu, s, w, qs, d8, gu, y,
+                                                                   qs_out, d8_out, Nh, nbe,
+                                                                   stride, K),
+                               true)
+                            : false) ||
+           ...);
+    return e;
+}
+
+template <class F>
+hipError_t launch_gate_up_fmt(const uint8_t *w, const uint8_t *q8_in, float *gu, float *y,
+                              uint8_t *q8_out, int64_t Nh, int64_t K, int num_cu, hipStream_t s)
+{
+    const uint32_t nbe = (uint32_t)(K / 256);
+    const int cpl = (int)((8u * nbe + 63u) / 64u);
+    const int8_t *qs = reinterpret_cast<const int8_t *>(q8_in);
+    const uint16_t *d8 = reinterpret_cast<const uint16_t *>(q8_in + (size_t)K);
+    uint16_t *d8_out = reinterpret_cast<uint16_t *>(q8_out + (size_t)Nh);
+    return dispatch_gate_up<F>(cpl, std::make_integer_sequence<int, 6>{}, num_cu, s, w, qs, d8,
+                               gu, y, q8_out, d8_out, (uint32_t)Nh, nbe,
+                               (uint32_t)kq_row_stride(F::TYPE, nbe), (uint32_t)K);
+}
+
 }  // namespace
 
 MmvqPlan plan_mmvq(int type, int64_t N, int64_t K, int nt, int num_cu)
@@ -870,6 +1006,30 @@ hipError_t launch_rmsnorm_mmvq(int type, const uint8_t *w, const float *x, const
     case KQT_Q6_K: return launch_fused_fmt<FmtQ6K>(w, x, gamma, eps, xn, q8, y, N, K, num_cu, s);
     case KQT_Q4_K: return launch_fused_fmt<FmtQ4K>(w, x, gamma, eps, xn, q8, y, N, K, num_cu, s);
     case KQT_Q5_K: return launch_fused_fmt<FmtQ5K>(w, x, gamma, eps, xn, q8, y, N, K, num_cu, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+bool gate_up_swiglu_fused(int64_t K)
+{
+    return fused_ok(1, (int)((K / 256 * 8 + 63) / 64));
+}
+
+hipError_t launch_gate_up_swiglu(int type, const uint8_t *w, const uint8_t *q8_in, float *gu,
+                                 float *y, uint8_t *q8_out, int64_t Nh, int64_t K, int num_cu,
+                                 hipStream_t s)
+{
+    if (!gate_up_swiglu_fused(K)) {
+        // the GEMV writes gu, then the SwiGLU producer reads its two halves
+        const hipError_t e = launch_mmvq(type, w, q8_in, gu, 2 * Nh, K, 1, num_cu, s);
+        if (e != hipSuccess)
+            return e;
+        return launch_swiglu_quant(gu, gu + Nh, y, q8_out, Nh, 1, s);
+    }
+    switch (type) {
+    case KQT_Q6_K: return launch_gate_up_fmt<FmtQ6K>(w, q8_in, gu, y, q8_out, Nh, K, num_cu, s);
+    case KQT_Q4_K: return launch_gate_up_fmt<FmtQ4K>(w, q8_in, gu, y, q8_out, Nh, K, num_cu, s);
+    case KQT_Q5_K: return launch_gate_up_fmt<FmtQ5K>(w, q8_in, gu, y, q8_out, Nh, K, num_cu, s);
     default: return hipErrorInvalidValue;
     }
 }

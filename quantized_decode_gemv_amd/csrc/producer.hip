@@ -31,7 +31,8 @@ __global__ __launch_bounds__(QWG) void quant_q8_kernel(const float4 *__restrict_
 
 // SwiGLU then q8 (D3-5 §3.2, the fused swiglu producer): y = (g / (1 + e^-g)) * u
 // in f32 -- IEEE division, the library expf -- stored and quantized from registers.
-// Each lane reads its g and u before it writes y, so y may be g or u itself.
+// Each lane reads its g and u before it writes y, so y may be g or u itself; y may
+// be null (not stored).
 __global__ __launch_bounds__(QWG) void swiglu_quant_kernel(const float4 *g, const float4 *u,
                                                            float4 *y, uint32_t *__restrict__ qs,
                                                            uint16_t *__restrict__ d8, uint32_t nf4)
@@ -48,7 +49,8 @@ __global__ __launch_bounds__(QWG) void swiglu_quant_kernel(const float4 *g, cons
     yv.w = (gv.w / (1.0f + expf(-gv.w))) * uv.w;
     const Q8Out o = quant_group8(yv);
     if (live) {
-        y[f] = yv;
+        if (y)
+            y[f] = yv;
         qs[f] = o.packed;
         if ((f & 7u) == 0)
             d8[f >> 3] = o.d16;

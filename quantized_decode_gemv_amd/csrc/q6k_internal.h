@@ -32,9 +32,17 @@ bool rmsnorm_mmvq_fused(int64_t K, int nt);
 hipError_t launch_rmsnorm_mmvq(int type, const uint8_t *w, const float *x, const float *gamma,
                                float eps, float *xn, uint8_t *q8, float *y, int64_t N, int64_t K,
                                int nt, int num_cu, hipStream_t s);
+// Form B: gate+up GEMV, SwiGLU and q8 of one token in one kernel when
+// gate_up_swiglu_fused(K), else the GEMV then the SwiGLU producer (same results bit
+// for bit). w: 2*Nh rows (gate, then up); gu: float [2*Nh]; y may be null.
+bool gate_up_swiglu_fused(int64_t K);
+hipError_t launch_gate_up_swiglu(int type, const uint8_t *w, const uint8_t *q8_in, float *gu,
+                                 float *y, uint8_t *q8_out, int64_t Nh, int64_t K, int num_cu,
+                                 hipStream_t s);
 hipError_t launch_quant(const float *x, uint8_t *q8, int64_t K, int nt, hipStream_t s);
 hipError_t launch_rmsnorm_quant(const float *x, const float *gamma, float eps, float *y,
                                 uint8_t *q8, int64_t K, int nt, hipStream_t s);
+// y may be null (not stored).
 hipError_t launch_swiglu_quant(const float *g, const float *u, float *y, uint8_t *q8, int64_t K,
                                int nt, hipStream_t s);
 hipError_t launch_repack(int type, const uint8_t *raw, uint8_t *dpl, int64_t N, int64_t K,

@@ -284,3 +284,26 @@ def test_kq_gemv_rejects_bad_arguments(qtype):
         assert _code(f, qtype, A, B, A + n, 4, 256, 1, 0) == E_ALIAS
     assert _code(q.mmvq_kq_q8_subdots, qtype, A, B, B, 4, 256, 1, 0) == E_ALIAS
     assert _code(q.repack_kq_dpl, qtype, A, A + 64, 1, 256, 0) == E_ALIAS
+
+
+def test_form_b_rejects_bad_arguments():
+    f = q.mmvq_kq_gate_up_swiglu_q8
+    E, F_ = 0x50000000, 0x60000000
+    t = q.KQ_Q4_K
+    assert _code(f, 11, A, B, C, None, D, 64, 256, 1, 0) == E_TYPE
+    assert _code(f, t, A, B, C, None, D, 48, 256, 1, 0) == E_SHAPE      # Nh % 32
+    assert _code(f, t, A, B, C, None, D, 64, 256, 2, 0) == E_SHAPE      # one token only
+    assert _code(f, t, A, B, C, None, D, 64, 288, 1, 0) == E_SHAPE      # K % 256
+    assert _code(f, t, A, B, C, None, D, 0, 256, 1, 0) == E_SHAPE
+    assert _code(f, t, None, B, C, None, D, 64, 256, 1, 0) == E_NULL
+    assert _code(f, t, A, B, None, None, D, 64, 256, 1, 0) == E_NULL
+    assert _code(f, t, A, B, C, None, None, 64, 256, 1, 0) == E_NULL
+    assert _code(f, t, A, B, C + 4, None, D, 64, 256, 1, 0) == E_ALIGN
+    assert _code(f, t, A, B, C, E + 8, D, 64, 256, 1, 0) == E_ALIGN
+    assert _code(f, t, A, B, A + 16, None, D, 64, 256, 1, 0) == E_ALIAS   # gu / w
+    assert _code(f, t, A, B, C, None, B + 16, 64, 256, 1, 0) == E_ALIAS   # q8_out / q8_in
+    assert _code(f, t, A, B, C, C + 256, D, 64, 256, 1, 0) == E_ALIAS    # y / gu
+    assert _code(f, t, A, B, C, None, C + 496, 64, 256, 1, 0) == E_ALIAS  # q8_out / gu
+    assert q.gate_up_swiglu_fused(13824, 5120) and not q.gate_up_swiglu_fused(64, 256 * 49)
+    with pytest.raises(q.Q6kError):
+        q.gate_up_swiglu_fused(48, 256)

@@ -25,10 +25,16 @@ def _buffers(producer, K, nt):
         up=torch.empty((nt, K), dtype=torch.float32, device=DEV),
         yn=torch.empty((nt, K), dtype=torch.float32, device=DEV),
         plane=torch.empty(q.q8_plane_bytes(K, nt), dtype=torch.uint8, device=DEV),
+        plane_out=torch.empty(max(q.q8_plane_bytes(2048, 1), 16), dtype=torch.uint8, device=DEV),
     )
 
 
 def _step(producer, b, W, y, N, K, nt):
+    if producer == "formb":   # rows [gate; up], the q8 plane of x as input
+        q.quant_q8(b["x"], b["plane"], K, nt)
+        q.mmvq_kq_gate_up_swiglu_q8(q.KQ_Q6_K, W, b["plane"], y.view(-1), b["yn"].view(-1)[:N // 2],
+                                    b["plane_out"], N // 2, K)
+        return
     if producer == "fused":
         q.mmvq_q6k_rmsnorm_q8(W, b["x"], b["gamma"], q6ksynth.RMS_EPS, b["yn"], b["plane"], y,
                               N, K, nt)
@@ -55,7 +61,8 @@ def _fill(producer, b, K, nt, seed):
 @pytest.mark.parametrize("producer,N,K,nt", [("rmsnorm", 4096, 5120, 1), ("rmsnorm", 2048, 5120, 4),
                                              ("swiglu", 1024, 13824, 1), ("quant", 64, 1024, 2),
                                              ("quant", 333, 256 * 97, 5),
-                                             ("fused", 4096, 5120, 1), ("fused", 1024, 5120, 2)])
+                                             ("fused", 4096, 5120, 1), ("fused", 1024, 5120, 2),
+                                             ("formb", 4096, 5120, 1)])
 def test_graph_replays_match_eager(producer, N, K, nt):
     raw = q6ksynth.raw_q6k(N, K, seed=N + K)
     W = dpl_from_raw(raw, N, K)
@@ -80,8 +87,10 @@ def test_graph_replays_match_eager(producer, N, K, nt):
         torch.cuda.synchronize()
         got = y.clone()
         plane_g = b["plane"].clone()
+        out_g = b["plane_out"].clone()
         _step(producer, b, W, y, N, K, nt)          # eager, same inputs
         torch.cuda.synchronize()
         assert torch.equal(b["plane"], plane_g), f"replay {rep}: q8 plane differs from eager"
+        assert torch.equal(b["plane_out"], out_g), f"replay {rep}: output plane differs"
         assert torch.equal(y, got), f"replay {rep}: y differs from eager"
     say(f"graph {producer} N={N} K={K} nt={nt}: 5 replays bitwise equal to eager")
