@@ -320,7 +320,7 @@ def main() -> int:
     achieved = content / (kern_us * 1e-6) / 1e9
     traffic = (None if formb or w.name != "lm_head"
                else recorded_traffic(f"{'fused' if fused else 'gemv'}_nt{nt}"))
-    plan = q.mmvq_plan(N, K, nt, torch.cuda.get_device_properties(0).multi_processor_count)
+    plan = q.mmvq_plan(N, K, nt, torch.cuda.get_device_properties(0).multi_processor_count, qt)
 
     out = {
         "metric": "q6_K MMVQ content GB/s and % of HBM peak; us per GEMV at lm_head shape",
