@@ -783,15 +783,26 @@ hipError_t dispatch_cpl(int cpl, const RowsCfg &c, std::integer_sequence<int, CP
 }
 
 // The fused RMSNorm -> q8 -> GEMV kernel is used for one token whose activation
-// operands stay in registers (up to 6 chunks per lane, K <= 12288). With more
-// tokens the norm work in every workgroup's prologue (one token's worth per token)
-// is no longer hidden behind the first weight rows, and the producer kernel
-// followed by the GEMV measured faster on lm_head 152064 x 5120 (nt = 2: equal;
-// nt = 3, 4: 2 and 4 us faster), so those shapes take the two kernels (with the
-// same results bit for bit).
+// operands stay in registers (up to FUSED_MAX_CPL chunks per lane, K <= 12288).
+// With more tokens the norm work in every workgroup's prologue (one token's worth
+// per token) is no longer hidden behind the first weight rows, and the producer
+// kernel followed by the GEMV measured faster on lm_head 152064 x 5120 (nt = 2:
+// equal; nt = 3, 4: 2 and 4 us faster), so those shapes take the two kernels (with
+// the same results bit for bit).
+constexpr int FUSED_MAX_CPL = 6;
+
 constexpr bool fused_ok(int nt, int cpl)
 {
-    return nt == 1 && cpl >= 1 && cpl <= 6;
+    return nt == 1 && cpl >= 1 && cpl <= FUSED_MAX_CPL;
+}
+
+// Form B keeps one token's activation operands in registers (hoisted), which the
+// row table does for up to 6 chunks per lane (K <= 12288).
+constexpr int GATE_UP_MAX_CPL = 6;
+
+constexpr bool gate_up_ok(int cpl)
+{
+    return cpl >= 1 && cpl <= GATE_UP_MAX_CPL;
 }
 
 struct FusedArgs {
@@ -905,8 +916,8 @@ hipError_t launch_fused_fmt(const uint8_t *w, const float *x, const float *gamma
     a.stride = (uint32_t)kq_row_stride(F::TYPE, nbe);
     a.K = (uint32_t)K;
     a.ldy = (uint32_t)N;
-    return dispatch_fused<F, 1>(cpl, c.depth, std::make_integer_sequence<int, 6>{}, num_cu,
-                                c.wg_per_cu, s, a);
+    return dispatch_fused<F, 1>(cpl, c.depth, std::make_integer_sequence<int, FUSED_MAX_CPL>{},
+                                num_cu, c.wg_per_cu, s, a);
 }
 
 template <class F, int CPL>
@@ -953,8 +964,8 @@ hipError_t launch_gate_up_fmt(const uint8_t *w, const uint8_t *q8_in, float *gu,
     const int8_t *qs = reinterpret_cast<const int8_t *>(q8_in);
     const uint16_t *d8 = reinterpret_cast<const uint16_t *>(q8_in + (size_t)K);
     uint16_t *d8_out = reinterpret_cast<uint16_t *>(q8_out + (size_t)Nh);
-    return dispatch_gate_up<F>(cpl, std::make_integer_sequence<int, 6>{}, num_cu, s, w, qs, d8,
-                               gu, y, q8_out, d8_out, (uint32_t)Nh, nbe,
+    return dispatch_gate_up<F>(cpl, std::make_integer_sequence<int, GATE_UP_MAX_CPL>{}, num_cu, s,
+                               w, qs, d8, gu, y, q8_out, d8_out, (uint32_t)Nh, nbe,
                                (uint32_t)kq_row_stride(F::TYPE, nbe), (uint32_t)K);
 }
 
@@ -1012,7 +1023,7 @@ hipError_t launch_rmsnorm_mmvq(int type, const uint8_t *w, const float *x, const
 
 bool gate_up_swiglu_fused(int64_t K)
 {
-    return fused_ok(1, (int)((K / 256 * 8 + 63) / 64));
+    return gate_up_ok((int)((K / 256 * 8 + 63) / 64));
 }
 
 hipError_t launch_gate_up_swiglu(int type, const uint8_t *w, const uint8_t *q8_in, float *gu,

@@ -57,10 +57,10 @@ __global__ __launch_bounds__(QWG) void swiglu_quant_kernel(const float4 *g, cons
     }
 }
 
-// One workgroup of NORM_WG threads per token row. Rows of up to NORM_WG * VPT
-// float4s are held in registers (x and gamma loaded once); longer rows are walked
-// twice from memory, summing in the same order. y is stored (when y is not null)
-// and quantized from registers, so the bytes equal quant_q8 applied to y.
+// One workgroup of NORM_WG threads per token row, with the sum order of
+// q6k_norm.h. Rows of up to NORM_WG * VPT float4s keep their x and gamma in
+// registers; longer rows are read again after the sum. y is stored (when y is not
+// null) and quantized from registers, so the bytes equal quant_q8 applied to y.
 template <int VPT>
 __global__ __launch_bounds__(NORM_WG) void rmsnorm_quant_regs(const float4 *__restrict__ x,
                                                               const float4 *__restrict__ g,
@@ -68,29 +68,28 @@ __global__ __launch_bounds__(NORM_WG) void rmsnorm_quant_regs(const float4 *__re
                                                               uint32_t *__restrict__ qs,
                                                               uint16_t *__restrict__ d8, uint32_t K)
 {
+    __shared__ double part[NORM_WG / 64];
     const uint32_t t = blockIdx.x;
     const uint32_t K4 = K / 4u;
-    const float4 *xr = x + (size_t)t * K4;
-    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+    const __amdgpu_buffer_rsrc_t rx = buf_desc(x + (size_t)t * K4, 16u * K4),
+                                 rg = buf_desc(g, 16u * K4);
     float4 xv[1][VPT], gv[VPT];
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
         const uint32_t f = threadIdx.x + v * NORM_WG;
-        xv[0][v] = f < K4 ? xr[f] : zero;
-        gv[v] = f < K4 ? g[f] : zero;
+        xv[0][v] = load_f4_desc(rx, f);
+        gv[v] = load_f4_desc(rg, f);
     }
-    __shared__ double part[NORM_WG / 64];
     float4 *yr = y ? y + (size_t)t * K4 : nullptr;
     uint32_t *qr = qs + (size_t)t * K4;
     uint16_t *dr = d8 + (size_t)t * (K / 32u);
-    norm_quant_rows<1, VPT>(xv, gv, K, eps, part,
-                            [&](int, uint32_t f, float4 yv, const Q8Out &o) {
-                                if (yr)
-                                    yr[f] = yv;
-                                qr[f] = o.packed;
-                                if ((f & 7u) == 0)
-                                    dr[f >> 3] = o.d16;
-                            });
+    norm_quant_rows<1, VPT>(xv, gv, K, eps, part, [&](int, uint32_t f, float4 yv, const Q8Out &o) {
+        if (yr)
+            yr[f] = yv;
+        qr[f] = o.packed;
+        if ((f & 7u) == 0)
+            dr[f >> 3] = o.d16;
+    });
 }
 
 __global__ __launch_bounds__(NORM_WG) void rmsnorm_quant_loop(const float4 *__restrict__ x,
@@ -99,20 +98,21 @@ __global__ __launch_bounds__(NORM_WG) void rmsnorm_quant_loop(const float4 *__re
                                                               uint32_t *__restrict__ qs,
                                                               uint16_t *__restrict__ d8, uint32_t K)
 {
+    __shared__ double part[NORM_WG / 64];
     const uint32_t t = blockIdx.x;
     const uint32_t K4 = K / 4u;
     const float4 *xr = x + (size_t)t * K4;
-    double ss[1] = {0.0};
-    for (uint32_t f = threadIdx.x; f < K4; f += NORM_WG)
-        ss[0] += sq_sum4(xr[f]);
-    __shared__ double part[NORM_WG / 64];
-    norm_block_sum<1>(ss, part);
-    const float r = norm_factor(ss[0], K, eps);
-
+    const uint32_t iters = (K4 + NORM_WG - 1) / NORM_WG;
+    double acc = 0.0;
+    for (uint32_t it = 0; it < iters; ++it) {
+        const uint32_t f = it * NORM_WG + threadIdx.x;
+        if (f < K4)
+            acc = sq_chain4(acc, xr[f]);
+    }
+    const float r = norm_factor(norm_block_total(acc, part), K, eps);
     float4 *yr = y ? y + (size_t)t * K4 : nullptr;
     uint32_t *qr = qs + (size_t)t * K4;
     uint16_t *dr = d8 + (size_t)t * (K / 32u);
-    const uint32_t iters = (K4 + NORM_WG - 1) / NORM_WG;
     for (uint32_t it = 0; it < iters; ++it) {
         const uint32_t f = it * NORM_WG + threadIdx.x;
         const bool live = f < K4;
