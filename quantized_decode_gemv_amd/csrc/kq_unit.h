@@ -34,7 +34,7 @@ namespace q6k {
 struct KqAct {
     uint4 xa, xb;   // the 16 int8 activations of each half
     float da, db;   // their q8 block scales (fp16 values, exact in f32)
-    int sa, sb;     // sums of xa, xb
+    float dsa, dsb; // da * sum(xa), db * sum(xb): exact (11-bit scale x 12-bit sum)
 };
 
 // Weight operands of one chunk.
@@ -59,25 +59,33 @@ __device__ __forceinline__ KqAct kq_load_act(const int8_t *__restrict__ qs_t,
     a.xb = *reinterpret_cast<const uint4 *>(qs_t + k + 32);
     a.da = f16_bits_to_f32(d8_t[blk]);
     a.db = f16_bits_to_f32(d8_t[blk + 1]);
-    a.sa = sum16_i8(a.xa);
-    a.sb = sum16_i8(a.xb);
+    a.dsa = a.da * (float)sum16_i8(a.xa);
+    a.dsb = a.db * (float)sum16_i8(a.xb);
     return a;
 }
 
-// 6-bit scale and min of sub-block s (0..7) from the 12 packed bytes (words p0:
-// bytes 0..3, p1: 4..7, p2: 8..11): for s < 4, sc = byte s & 63, m = byte s+4 & 63;
-// for s >= 4 (i = s - 4), sc = (byte i+8 & 15) | (byte i >> 6) << 4 and
-// m = (byte i+8 >> 4) | (byte i+4 >> 6) << 4. s is the same for every chunk of a
-// lane, so the selects below take per-lane constant conditions.
-__device__ __forceinline__ void kq_scale_min(uint3 p, uint32_t s, int &sc, int &m)
+// 6-bit scales and mins of the chunk's sub-blocks s = 2j and 2j + 1 (j = (Q >> 1) & 3)
+// from the 12 packed bytes (words p0: bytes 0..3, p1: 4..7, p2: 8..11): for s < 4,
+// sc = byte s & 63 and m = byte s+4 & 63; for s >= 4 (i = s - 4),
+// sc = (byte i+8 & 15) | (byte i >> 6) << 4 and m = (byte i+8 >> 4) | (byte i+4 >> 6) << 4.
+// Both forms are "a low field of width 6 or 4, or-ed with a high field of width 0 or 2
+// shifted to bit 4", so each value is two bitfield extracts with per-lane offsets and
+// widths (a width-0 extract is 0).
+__device__ __forceinline__ void kq_scale_min2(uint3 p, uint32_t Q, int &sca, int &ma, int &scb,
+                                              int &mb)
 {
-    const uint32_t sh = 8u * (s & 3u);
-    const uint32_t lo_sc = (p.x >> sh) & 63u, lo_m = (p.y >> sh) & 63u;
-    const uint32_t hi_sc = ((p.z >> sh) & 15u) | (((p.x >> (sh + 6u)) & 3u) << 4);
-    const uint32_t hi_m = ((p.z >> (sh + 4u)) & 15u) | (((p.y >> (sh + 6u)) & 3u) << 4);
-    const bool hi = s >= 4u;
-    sc = (int)(hi ? hi_sc : lo_sc);
-    m = (int)(hi ? hi_m : lo_m);
+    const uint32_t j = (Q >> 1) & 3u;
+    const bool hi = j >= 2u;
+    const uint32_t o = 16u * (j & 1u);        // bit offset of byte (2j) & 3
+    const uint32_t A = hi ? p.z : p.x, Am = hi ? p.z : p.y;
+    const uint32_t wl = hi ? 4u : 6u, om = hi ? 4u : 0u, wh = hi ? 2u : 0u;
+    const auto bfe = [](uint32_t v, uint32_t off, uint32_t w) {
+        return __builtin_amdgcn_ubfe(v, off, w);
+    };
+    sca = (int)(bfe(A, o, wl) | (bfe(p.x, o + 6u, wh) << 4));
+    scb = (int)(bfe(A, o + 8u, wl) | (bfe(p.x, o + 14u, wh) << 4));
+    ma = (int)(bfe(Am, o + om, wl) | (bfe(p.y, o + 6u, wh) << 4));
+    mb = (int)(bfe(Am, o + 8u + om, wl) | (bfe(p.y, o + 14u, wh) << 4));
 }
 
 // The chunk's four codes per 32-bit word: low nibbles (sub-block 2j) or high
@@ -106,11 +114,10 @@ __device__ __forceinline__ void kq_chunk_dots(const KqW &w, const KqAct &a, uint
                                               int &Db)
 {
     const uint32_t sh = 2u * ((Q >> 1) & 3u);
-    int da = 0, db = 0;
     uint32_t h;
     h = Q5 ? w.qh.x >> sh : 0u;
-    da = __builtin_amdgcn_sdot4((int)kq_codes_lo<Q5>(w.qs.x, h), (int)a.xa.x, da, false);
-    db = __builtin_amdgcn_sdot4((int)kq_codes_hi<Q5>(w.qs.x, h), (int)a.xb.x, db, false);
+    int da = sdot4_from0((int)kq_codes_lo<Q5>(w.qs.x, h), (int)a.xa.x);
+    int db = sdot4_from0((int)kq_codes_hi<Q5>(w.qs.x, h), (int)a.xb.x);
     h = Q5 ? w.qh.y >> sh : 0u;
     da = __builtin_amdgcn_sdot4((int)kq_codes_lo<Q5>(w.qs.y, h), (int)a.xa.y, da, false);
     db = __builtin_amdgcn_sdot4((int)kq_codes_hi<Q5>(w.qs.y, h), (int)a.xb.y, db, false);
@@ -125,20 +132,19 @@ __device__ __forceinline__ void kq_chunk_dots(const KqW &w, const KqAct &a, uint
 }
 
 // acc + d * (d8a * sca*Dqa + d8b * scb*Dqb) - dmin * (d8a * ma*Sxa + d8b * mb*Sxb),
-// d and dmin passed in (zero drops the chunk). sc*Dq (|Dq| <= 16*31*128) and m*Sx are
-// exact integers below 2^23, so their f32 conversions are exact; every multiply-add
-// is written out.
+// d and dmin passed in (zero drops the chunk). sc*Dq (|Dq| <= 16*31*128) is an exact
+// integer below 2^23, so its f32 conversion is exact; d8*Sx is exact in f32 (an fp16
+// value times a 12-bit sum), so m * (d8*Sx) rounds the same real number d8*(m*Sx) does,
+// once. Every multiply-add is written out.
 template <bool Q5>
 __device__ __forceinline__ float kq_chunk_accumulate(float acc, const KqW &w, const KqAct &a,
                                                      uint32_t Q, float d, float dmin)
 {
     int Da, Db, sca, ma, scb, mb;
     kq_chunk_dots<Q5>(w, a, Q, Da, Db);
-    const uint32_t s = 2u * ((Q >> 1) & 3u);
-    kq_scale_min(w.sc, s, sca, ma);
-    kq_scale_min(w.sc, s + 1u, scb, mb);
+    kq_scale_min2(w.sc, Q, sca, ma, scb, mb);
     const float pd = __builtin_fmaf(a.da, (float)__mul24(sca, Da), a.db * (float)__mul24(scb, Db));
-    const float pm = __builtin_fmaf(a.da, (float)__mul24(ma, a.sa), a.db * (float)__mul24(mb, a.sb));
+    const float pm = __builtin_fmaf((float)ma, a.dsa, (float)mb * a.dsb);
     return __builtin_fmaf(-dmin, pm, __builtin_fmaf(d, pd, acc));
 }
 
@@ -180,11 +186,23 @@ struct FmtKq {
         return kq_load_act(qs_t, d8_t, Q);
     }
 
+    // live = false drops the chunk (d = dmin = 0); callers whose operands were
+    // dropped already pass true
     __device__ static float accumulate(float acc, const W &w, const Act &a, uint32_t Q, bool live)
     {
         const float d = live ? f16_bits_to_f32(w.dm & 0xFFFFu) : 0.0f;
         const float dmin = live ? f16_bits_to_f32(w.dm >> 16) : 0.0f;
         return kq_chunk_accumulate<Q5>(acc, w, a, Q, d, dmin);
+    }
+
+    // Operands that make the chunk contribute exactly zero: the block scales, which
+    // multiply everything else, set to 0 (the weights are finite).
+    __device__ static void drop(Act &a)
+    {
+        a.da = 0.0f;
+        a.db = 0.0f;
+        a.dsa = 0.0f;
+        a.dsb = 0.0f;
     }
 };
 

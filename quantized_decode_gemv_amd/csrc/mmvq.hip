@@ -158,7 +158,8 @@ __device__ __forceinline__ void lane_chunks(LaneState<F, NT, CPL, HOIST> &st, ui
 }
 
 // qs, d8: the activation rows (global memory or LDS), token t at qs + t * K and
-// d8 + t * (K / 32).
+// d8 + t * (K / 32). A chunk past the row gets dropped operands (F::drop), so the
+// row loop needs no per-row select for it.
 template <class F, int NT, int CPL>
 __device__ __forceinline__ void lane_acts(LaneState<F, NT, CPL, true> &st, const int8_t *qs,
                                           const uint16_t *d8, uint32_t K)
@@ -166,8 +167,11 @@ __device__ __forceinline__ void lane_acts(LaneState<F, NT, CPL, true> &st, const
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < NT; ++t) {
             st.act[i][t] = F::act(qs + (size_t)t * K, d8 + (size_t)t * (K / 32), st.Q[i]);
+            if (!st.live[i])
+                F::drop(st.act[i][t]);
+        }
     }
 }
 
@@ -210,7 +214,8 @@ __device__ __forceinline__ float row_total(const typename F::W (&src)[CPL],
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             if constexpr (HOIST) {
-                acc[t] = F::accumulate(acc[t], src[i], st.act[i][t], st.Q[i], st.live[i]);
+                // dead chunks' operands were dropped in lane_acts
+                acc[t] = F::accumulate(acc[t], src[i], st.act[i][t], st.Q[i], true);
             } else {
                 const typename F::Act a =
                     F::act(qs + (size_t)t * K, d8 + (size_t)t * (K / 32), st.Q[i]);
@@ -455,13 +460,7 @@ __global__ __launch_bounds__(WG) void mmvq_rmsnorm_rows(
     __syncthreads();
     // the activation rows in LDS have the layout of the q8 plane: token t at
     // s_qs[t] (K bytes) and s_d8[t]
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-            st.act[i][t] = F::act(reinterpret_cast<const int8_t *>(&s_qs[t][0]), &s_d8[t][0],
-                                  st.Q[i]);
-    }
+    lane_acts(st, reinterpret_cast<const int8_t *>(&s_qs[0][0]), &s_d8[0][0], 4u * K4_MAX);
     if (wave >= N)
         return;
     prime_rows<F, NT, CPL, PRE, DEPTH, true>(A, B, Cb, w, wave, nw, N, stride, st);
@@ -689,7 +688,7 @@ struct RowsCfg {
 
 constexpr RowsCfg rows_cfg(int type, int nt, int cpl)
 {
-    const bool q6 = type == KQT_Q6_K;
+    const bool q6 = type == KQT_Q6_K, q4 = type == KQT_Q4_K;
     if (nt == 1) {
         if (cpl == 1)
             return {2, true, 4};
@@ -697,21 +696,43 @@ constexpr RowsCfg rows_cfg(int type, int nt, int cpl)
             return q6 ? RowsCfg{2, true, 2} : RowsCfg{3, true, 2};
         if (cpl == 3)
             return q6 ? RowsCfg{3, true, 1} : RowsCfg{2, true, 2};
-        if (cpl <= 6 || (cpl == 7 && type != KQT_Q5_K))
+        if (cpl <= 6 || (cpl == 7 && q4) || (cpl == 11 && q6))
             return {2, true, 1};
-        return {1, false, 2};
+        return {1, true, 2};
     }
     if (cpl == 1)
         return {3, true, 2};
     if (cpl == 2)
         return (nt == 2 && !q6) ? RowsCfg{3, true, 2} : RowsCfg{2, true, 2};
-    if (cpl == 3)
+    if (cpl == 4 && nt == 2 && q6)
+        return {2, true, 1};
+    if (cpl <= 6)
         return {2, true, 2};
-    if (cpl == 4)
-        return (nt == 2 && q6) ? RowsCfg{2, true, 1} : RowsCfg{2, true, 2};
-    if (nt * cpl <= 6)
-        return {2, true, 2};
-    return {1, false, 2};
+    // 7 or more chunks per lane: at most two tokens per launch (tokens_per_launch),
+    // except q6_K and q4_K at 7
+    if (nt == 2) {
+        if (q6)
+            return cpl == 7 ? RowsCfg{2, true, 1} : RowsCfg{1, true, 2};
+        return (q4 || cpl <= 10) ? RowsCfg{2, true, 1} : RowsCfg{1, true, 2};
+    }
+    return q6 ? RowsCfg{1, true, 2} : RowsCfg{2, true, 1};
+}
+
+// Token columns per launch: each launch reads the weights once for its columns, but
+// every column's activation operands live in registers across the whole row, and
+// past six chunks per lane four columns no longer fit them. There one or two columns
+// per launch, reading the weights two or four times, measured faster than the
+// four-column kernels (graph-replayed sweeps of 4096-row matrices, 7..12 chunks per
+// lane: e.g. q6_K at 10 chunks 60 us for four columns in one launch, 33 us in two).
+constexpr int tokens_per_launch(int type, int cpl)
+{
+    if (cpl <= 6)
+        return MAX_NT_KERNEL;
+    if (type == KQT_Q6_K)
+        return cpl == 7 ? 4 : 2;
+    if (type == KQT_Q4_K)
+        return cpl == 7 ? 4 : (cpl <= 10 ? 2 : 1);
+    return cpl <= 8 ? 2 : 1;
 }
 
 struct GemvArgs {
@@ -765,11 +786,14 @@ hipError_t launch(Kern kern, int num_cu, int wg_per_cu, hipStream_t s, GemvArgs 
 template <class F, int NT, int CPL>
 hipError_t launch_cpl(const RowsCfg &c, int num_cu, hipStream_t s, const GemvArgs &a)
 {
-    // the one (depth, hoist) pair rows_cfg picks for this type, NT and CPL is built
+    // the one (depth, hoist) pair rows_cfg picks for this type, NT and CPL is built,
+    // for the token counts a launch of this CPL can have
     constexpr RowsCfg k = rows_cfg(F::TYPE, NT, CPL);
-    if (c.depth != k.depth || c.hoist != k.hoist)
-        return hipErrorInvalidValue;
-    return launch(mmvq_rows<F, NT, CPL, k.depth, k.hoist>, num_cu, c.wg_per_cu, s, a);
+    if constexpr (NT <= tokens_per_launch(F::TYPE, CPL)) {
+        if (c.depth == k.depth && c.hoist == k.hoist)
+            return launch(mmvq_rows<F, NT, CPL, k.depth, k.hoist>, num_cu, c.wg_per_cu, s, a);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <class F, int NT, int... CPLS>
@@ -858,8 +882,9 @@ hipError_t launch_mmvq_fmt(const uint8_t *w, const uint8_t *q8, float *y, int64_
     const int8_t *qs = reinterpret_cast<const int8_t *>(q8);
     const uint16_t *d8 = reinterpret_cast<const uint16_t *>(q8 + (size_t)nt * K);
     const int cpl = (int)((8u * nbe + 63u) / 64u);
-    for (int t0 = 0; t0 < nt; t0 += MAX_NT_KERNEL) {
-        const int n = nt - t0 < MAX_NT_KERNEL ? nt - t0 : MAX_NT_KERNEL;
+    const int step = cpl <= MAX_CPL ? tokens_per_launch(F::TYPE, cpl) : MAX_NT_KERNEL;
+    for (int t0 = 0; t0 < nt; t0 += step) {
+        const int n = nt - t0 < step ? nt - t0 : step;
         GemvArgs a;
         a.w = w;
         a.qs = qs + (size_t)t0 * K;
@@ -977,8 +1002,9 @@ MmvqPlan plan_mmvq(int type, int64_t N, int64_t K, int nt, int num_cu)
     const int64_t nbe = K / 256;
     p.cpl = (int)((8 * nbe + 63) / 64);
     p.unrolled = p.cpl <= MAX_CPL;
-    p.launches = (nt + MAX_NT_KERNEL - 1) / MAX_NT_KERNEL;
-    const int nt0 = nt < MAX_NT_KERNEL ? nt : MAX_NT_KERNEL;
+    const int step = p.unrolled ? tokens_per_launch(type, p.cpl) : MAX_NT_KERNEL;
+    p.launches = (nt + step - 1) / step;
+    const int nt0 = nt < step ? nt : step;
     const RowsCfg c = p.unrolled ? rows_cfg(type, nt0, p.cpl) : RowsCfg{1, false, 2};
     p.hoist = p.unrolled && c.hoist;
     p.depth = c.depth;

@@ -15,7 +15,7 @@ struct MmvqPlan {
     int cpl = 0;            // low-bit chunks per lane per row
     bool unrolled = false;  // a fixed-CPL kernel (else the generic stepping kernel)
     bool hoist = false;     // activation operands held in registers across rows
-    int launches = 0;       // one launch per group of up to 4 token columns
+    int launches = 0;       // one launch per group of token columns (up to 4)
     int depth = 1;          // rows in flight per wave
 };
 

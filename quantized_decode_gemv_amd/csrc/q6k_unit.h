@@ -55,6 +55,22 @@ __device__ __forceinline__ int sum16_i8(uint4 v)
     return __builtin_amdgcn_sdot4((int)v.w, 0x01010101, s, false);
 }
 
+// c + the signed int8 dot of a and b, as the three-address v_dot4_i32_i8. The
+// builtin selects the two-address accumulate-in-place form, which needs a copy of c
+// first whenever c lives on (a hoisted activation sum, a zero).
+__device__ __forceinline__ int sdot4_to(int a, int b, int c)
+{
+    int r;
+    asm("v_dot4_i32_i8 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ int sdot4_from0(int a, int b)
+{
+    int r;
+    asm("v_dot4_i32_i8 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // qs_t: int8 activations of one token (K entries); d8_t: its fp16 block scales.
 __device__ __forceinline__ ChunkAct load_act(const int8_t *__restrict__ qs_t,
                                              const uint16_t *__restrict__ d8_t, uint32_t Q)
@@ -85,15 +101,18 @@ __device__ __forceinline__ ChunkW load_w(const uint8_t *__restrict__ row, uint32
 }
 
 // Four codes per 32-bit word: low nibbles (unit s) or high nibbles (unit s + 2) of
-// the low-bit word, with the matching 2-bit fields of the high-bit word placed at
-// bits 4..5 of each byte. h_sh is the high-bit word shifted right by 2s.
-__device__ __forceinline__ uint32_t codes_lo(uint32_t l, uint32_t h_sh)
+// the low-bit word l, with the matching 2-bit fields at bits 4..5 of each byte. hm is
+// the high-bit word masked to this chunk's two fields (bits 2s..2s+1 and 2s+4..2s+5
+// of each byte); up = 4 - 2s moves the first to bits 4..5, 2s the second. Each is
+// one bitfield insert: bits 0..3 of every byte from l (or l >> 4), bits 4..7 from the
+// shifted fields, whose other bits are zero there.
+__device__ __forceinline__ uint32_t codes_lo(uint32_t l, uint32_t hm, uint32_t up)
 {
-    return (l & 0x0F0F0F0Fu) | ((h_sh << 4) & 0x30303030u);
+    return (l & 0x0F0F0F0Fu) | ((hm << up) & 0xF0F0F0F0u);
 }
-__device__ __forceinline__ uint32_t codes_hi(uint32_t l, uint32_t h_sh)
+__device__ __forceinline__ uint32_t codes_hi(uint32_t l, uint32_t hm, uint32_t sh)
 {
-    return ((l >> 4) & 0x0F0F0F0Fu) | (h_sh & 0x30303030u);
+    return ((l >> 4) & 0x0F0F0F0Fu) | ((hm >> sh) & 0xF0F0F0F0u);
 }
 
 // The chunk's two exact sub-block dots sum (q - 32) * x8: the dot of the unsigned
@@ -101,21 +120,20 @@ __device__ __forceinline__ uint32_t codes_hi(uint32_t l, uint32_t h_sh)
 __device__ __forceinline__ void chunk_dots(const ChunkW &w, const ChunkAct &a, uint32_t Q,
                                            int &Da, int &Db)
 {
-    const uint32_t sh = 2u * ((Q >> 1) & 1u);
-    int da = a.na, db = a.nb;
-    uint32_t h;
-    h = w.qh.x >> sh;
-    da = __builtin_amdgcn_sdot4((int)codes_lo(w.ql.x, h), (int)a.xa.x, da, false);
-    db = __builtin_amdgcn_sdot4((int)codes_hi(w.ql.x, h), (int)a.xb.x, db, false);
-    h = w.qh.y >> sh;
-    da = __builtin_amdgcn_sdot4((int)codes_lo(w.ql.y, h), (int)a.xa.y, da, false);
-    db = __builtin_amdgcn_sdot4((int)codes_hi(w.ql.y, h), (int)a.xb.y, db, false);
-    h = w.qh.z >> sh;
-    da = __builtin_amdgcn_sdot4((int)codes_lo(w.ql.z, h), (int)a.xa.z, da, false);
-    db = __builtin_amdgcn_sdot4((int)codes_hi(w.ql.z, h), (int)a.xb.z, db, false);
-    h = w.qh.w >> sh;
-    da = __builtin_amdgcn_sdot4((int)codes_lo(w.ql.w, h), (int)a.xa.w, da, false);
-    db = __builtin_amdgcn_sdot4((int)codes_hi(w.ql.w, h), (int)a.xb.w, db, false);
+    const uint32_t sh = 2u * ((Q >> 1) & 1u), up = 4u - sh;
+    const uint32_t M = 0x33333333u << sh;
+    uint32_t hm = w.qh.x & M;
+    int da = sdot4_to((int)codes_lo(w.ql.x, hm, up), (int)a.xa.x, a.na);
+    int db = sdot4_to((int)codes_hi(w.ql.x, hm, sh), (int)a.xb.x, a.nb);
+    hm = w.qh.y & M;
+    da = __builtin_amdgcn_sdot4((int)codes_lo(w.ql.y, hm, up), (int)a.xa.y, da, false);
+    db = __builtin_amdgcn_sdot4((int)codes_hi(w.ql.y, hm, sh), (int)a.xb.y, db, false);
+    hm = w.qh.z & M;
+    da = __builtin_amdgcn_sdot4((int)codes_lo(w.ql.z, hm, up), (int)a.xa.z, da, false);
+    db = __builtin_amdgcn_sdot4((int)codes_hi(w.ql.z, hm, sh), (int)a.xb.z, db, false);
+    hm = w.qh.w & M;
+    da = __builtin_amdgcn_sdot4((int)codes_lo(w.ql.w, hm, up), (int)a.xa.w, da, false);
+    db = __builtin_amdgcn_sdot4((int)codes_hi(w.ql.w, hm, sh), (int)a.xb.w, db, false);
     Da = da;
     Db = db;
 }
@@ -193,10 +211,20 @@ struct FmtQ6K {
         return load_act(qs_t, d8_t, Q);
     }
 
+    // live = false drops the chunk (d = 0); callers whose operands were dropped
+    // already pass true
     __device__ static float accumulate(float acc, const W &w, const Act &a, uint32_t Q, bool live)
     {
-        const float d = live ? f16_bits_to_f32(w.d) : 0.0f;   // 0 drops the chunk
+        const float d = live ? f16_bits_to_f32(w.d) : 0.0f;
         return chunk_accumulate(acc, w, a, Q, d);
+    }
+
+    // Operands that make the chunk contribute exactly zero: the block scales, which
+    // multiply everything else, set to 0 (the weights are finite).
+    __device__ static void drop(Act &a)
+    {
+        a.da = 0.0f;
+        a.db = 0.0f;
     }
 };
 
