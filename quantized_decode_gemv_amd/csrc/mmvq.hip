@@ -693,7 +693,7 @@ constexpr RowsCfg rows_cfg(int type, int nt, int cpl)
         if (cpl == 1)
             return {2, true, 4};
         if (cpl == 2)
-            return q6 ? RowsCfg{2, true, 2} : RowsCfg{3, true, 2};
+            return {2, true, 2};
         if (cpl == 3)
             return q6 ? RowsCfg{3, true, 1} : RowsCfg{2, true, 2};
         if (cpl <= 6 || (cpl == 7 && q4) || (cpl == 11 && q6))
