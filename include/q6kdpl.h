@@ -248,9 +248,9 @@ int mmvq_kq_q8_subdots(int type, const void *w_dpl, const void *q8, int32_t *dot
  * out6[0] = workgroups per launch (256 threads each; a launch uses fewer where the
  * kernel's registers fit fewer workgroups per CU), out6[1] = low-bit chunks per
  * lane per row, out6[2] = 1 for a fixed-length kernel (0: the generic stepping
- * kernel), out6[3] = 1 when activation operands stay in registers across rows,
- * out6[4] = launches (one per group of token columns: up to 4, or 2 or 1 on rows
- * of more than 7 low-bit chunks per lane, depending on the type), out6[5] = rows in
+ * kernel), out6[3] = where activation operands live across rows (0: re-read from
+ * the q8 plane per row, 1: registers, 2: staged once per workgroup in LDS),
+ * out6[4] = launches (one per group of up to 4 token columns), out6[5] = rows in
  * flight per wave. Host only. */
 int q6k_mmvq_plan(int64_t N, int64_t K, int nt, int num_cu, int32_t *out6);
 

@@ -229,8 +229,10 @@ def mmvq_q6k_q8_subdots(w_dpl, q8, dots, N: int, K: int, nt: int, stream=None) -
 def mmvq_plan(N: int, K: int, nt: int, num_cu: int, qtype: int = 14) -> dict:
     out = (ctypes.c_int32 * 6)()
     _call("kq_mmvq_plan", qtype, N, K, nt, num_cu, ctypes.addressof(out))
-    return dict(grid=out[0], cpl=out[1], unrolled=bool(out[2]), hoist=bool(out[3]),
-                launches=out[4], depth=out[5])
+    # act_mode: 0 activation operands re-read per row, 1 held in registers ("hoist"),
+    # 2 staged in LDS once per workgroup
+    return dict(grid=out[0], cpl=out[1], unrolled=bool(out[2]), hoist=out[3] == 1,
+                act_mode=out[3], launches=out[4], depth=out[5])
 
 
 # --- by weight type (q4_K, q5_K, q6_K) ---------------------------------------------

@@ -204,6 +204,28 @@ struct FmtKq {
         a.dsa = 0.0f;
         a.dsb = 0.0f;
     }
+
+    // The operands as three 16-byte words (LDS staging) and back; all-zero words give
+    // operands that contribute exactly zero.
+    __device__ static void to_words(const Act &a, uint4 &xa, uint4 &xb, uint4 &sc)
+    {
+        xa = a.xa;
+        xb = a.xb;
+        sc = make_uint4(__builtin_bit_cast(uint32_t, a.da), __builtin_bit_cast(uint32_t, a.db),
+                        __builtin_bit_cast(uint32_t, a.dsa), __builtin_bit_cast(uint32_t, a.dsb));
+    }
+    __device__ static Act from_words(const uint4 &xa, const uint4 &xb, const uint4 &sc)
+    {
+        const uint32_t s0 = sc.x, s1 = sc.y, s2 = sc.z, s3 = sc.w;
+        Act a;
+        a.xa = xa;
+        a.xb = xb;
+        a.da = __builtin_bit_cast(float, s0);
+        a.db = __builtin_bit_cast(float, s1);
+        a.dsa = __builtin_bit_cast(float, s2);
+        a.dsb = __builtin_bit_cast(float, s3);
+        return a;
+    }
 };
 
 using FmtQ4K = FmtKq<false>;

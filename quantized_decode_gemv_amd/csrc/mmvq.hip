@@ -38,6 +38,7 @@
 // units of all rows of any shape it is launched on (D4-2 §2: a dispatch that routes
 // a shape to a kernel covering fewer units silently drops work).
 
+#include <map>
 #include <mutex>
 #include <unordered_map>
 
@@ -134,17 +135,28 @@ __device__ __forceinline__ bool stores_token(uint32_t lane, uint32_t &t)
     return lane < (uint32_t)NT;
 }
 
+// Where a lane's activation operands live across rows: re-read from the q8 plane
+// per row (ACT_GLOBAL), held in registers (ACT_REGS), or staged once per workgroup
+// in LDS and read per row (ACT_LDS; for rows whose operands do not fit registers).
+enum ActMode : int { ACT_GLOBAL = 0, ACT_REGS = 1, ACT_LDS = 2 };
+
 // Per-lane state that is the same for every row a wave visits.
-template <class F, int NT, int CPL, bool HOIST>
+template <class F, int NT, int CPL, int AM>
 struct LaneState {
     typename F::Offs off[CPL];
     uint32_t Q[CPL];        // chunk index (clamped to the last chunk past the row end)
     bool live[CPL];         // false: duplicate load, contributes 0
-    typename F::Act act[HOIST ? CPL : 1][NT];
+    typename F::Act act[AM == ACT_REGS ? CPL : 1][NT];
+    // ACT_LDS: three planes (first halves, second halves, scalars) of `plane` 16-byte
+    // entries; token t's entry of chunk slot i at t * tstride + ent[i], where a slot
+    // past the row points at the token's all-zero entry
+    uint32_t ent[AM == ACT_LDS ? CPL : 1];
+    const uint4 *lds;
+    uint32_t plane, tstride;
 };
 
-template <class F, int NT, int CPL, bool HOIST>
-__device__ __forceinline__ void lane_chunks(LaneState<F, NT, CPL, HOIST> &st, uint32_t lane,
+template <class F, int NT, int CPL, int AM>
+__device__ __forceinline__ void lane_chunks(LaneState<F, NT, CPL, AM> &st, uint32_t lane,
                                             uint32_t nbe)
 {
     const uint32_t C = 8u * nbe;
@@ -161,7 +173,7 @@ __device__ __forceinline__ void lane_chunks(LaneState<F, NT, CPL, HOIST> &st, ui
 // d8 + t * (K / 32). A chunk past the row gets dropped operands (F::drop), so the
 // row loop needs no per-row select for it.
 template <class F, int NT, int CPL>
-__device__ __forceinline__ void lane_acts(LaneState<F, NT, CPL, true> &st, const int8_t *qs,
+__device__ __forceinline__ void lane_acts(LaneState<F, NT, CPL, ACT_REGS> &st, const int8_t *qs,
                                           const uint16_t *d8, uint32_t K)
 {
 #pragma unroll
@@ -175,20 +187,20 @@ __device__ __forceinline__ void lane_acts(LaneState<F, NT, CPL, true> &st, const
     }
 }
 
-template <class F, int NT, int CPL, bool HOIST>
-__device__ __forceinline__ void lane_init(LaneState<F, NT, CPL, HOIST> &st, uint32_t lane,
+template <class F, int NT, int CPL, int AM>
+__device__ __forceinline__ void lane_init(LaneState<F, NT, CPL, AM> &st, uint32_t lane,
                                           uint32_t nbe, const int8_t *qs, const uint16_t *d8,
                                           uint32_t K)
 {
     lane_chunks(st, lane, nbe);
-    if constexpr (HOIST)
+    if constexpr (AM == ACT_REGS)
         lane_acts(st, qs, d8, K);
 }
 
-template <class F, int NT, int CPL, bool HOIST>
+template <class F, int NT, int CPL, int AM>
 __device__ __forceinline__ void load_row(typename F::W (&dst)[CPL], const uint8_t *w,
                                          uint32_t row, uint32_t N, uint32_t stride,
-                                         const LaneState<F, NT, CPL, HOIST> &st)
+                                         const LaneState<F, NT, CPL, AM> &st)
 {
     const bool real = row < N;
     const __amdgpu_buffer_rsrc_t r = row_desc(w, real ? row : 0u, stride, real);
@@ -197,14 +209,26 @@ __device__ __forceinline__ void load_row(typename F::W (&dst)[CPL], const uint8_
         dst[i] = F::load(r, st.off[i]);
 }
 
+// A zero the compiler cannot see through, different for every row (row & 0 by an
+// instruction it does not evaluate): ACT_LDS reads indexed with it stay inside the
+// row loop, where they would otherwise be hoisted into registers, which is what that
+// mode is there to avoid.
+__device__ __forceinline__ uint32_t row_zero(uint32_t row)
+{
+    uint32_t z;
+    asm("v_and_b32 %0, 0, %1" : "=v"(z) : "v"(row));
+    return z;
+}
+
 // The row's totals for its token columns: lane l holds the total of token
 // (l & 3) (NT = 2: l & 1; NT = 1: every lane the only token's).
-template <class F, int NT, int CPL, bool HOIST>
+template <class F, int NT, int CPL, int AM>
 __device__ __forceinline__ float row_total(const typename F::W (&src)[CPL],
-                                           const LaneState<F, NT, CPL, HOIST> &st,
+                                           const LaneState<F, NT, CPL, AM> &st,
                                            const int8_t *qs, const uint16_t *d8, uint32_t K,
-                                           uint32_t lane)
+                                           uint32_t lane, uint32_t row = 0)
 {
+    const uint32_t z = AM == ACT_LDS ? row_zero(row) : 0u;
     float acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -213,9 +237,15 @@ __device__ __forceinline__ float row_total(const typename F::W (&src)[CPL],
     for (int i = 0; i < CPL; ++i) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            if constexpr (HOIST) {
+            if constexpr (AM == ACT_REGS) {
                 // dead chunks' operands were dropped in lane_acts
                 acc[t] = F::accumulate(acc[t], src[i], st.act[i][t], st.Q[i], true);
+            } else if constexpr (AM == ACT_LDS) {
+                // dead chunks read the all-zero entry
+                const uint32_t e = t * st.tstride + st.ent[i] + z;
+                const typename F::Act a =
+                    F::from_words(st.lds[e], st.lds[st.plane + e], st.lds[2u * st.plane + e]);
+                acc[t] = F::accumulate(acc[t], src[i], a, st.Q[i], true);
             } else {
                 const typename F::Act a =
                     F::act(qs + (size_t)t * K, d8 + (size_t)t * (K / 32), st.Q[i]);
@@ -226,13 +256,13 @@ __device__ __forceinline__ float row_total(const typename F::W (&src)[CPL],
     return reduce_tokens<NT>(acc, lane);
 }
 
-template <class F, int NT, int CPL, bool HOIST>
+template <class F, int NT, int CPL, int AM>
 __device__ __forceinline__ void finish_row(const typename F::W (&src)[CPL],
-                                           const LaneState<F, NT, CPL, HOIST> &st,
+                                           const LaneState<F, NT, CPL, AM> &st,
                                            const int8_t *qs, const uint16_t *d8, uint32_t K,
                                            float *y, uint32_t ldy, uint32_t row, uint32_t lane)
 {
-    const float s = row_total<F, NT, CPL, HOIST>(src, st, qs, d8, K, lane);
+    const float s = row_total<F, NT, CPL, AM>(src, st, qs, d8, K, lane, row);
     uint32_t t;
     if (stores_token<NT>(lane, t))
         y[(size_t)t * ldy + row] = s;
@@ -240,11 +270,11 @@ __device__ __forceinline__ void finish_row(const typename F::W (&src)[CPL],
 
 // Requests rows FROM .. TO - 1 of a wave's walk (row, row + nw, ...), the first
 // DEPTH of which go to A, B and Cb in that order.
-template <class F, int NT, int CPL, int FROM, int TO, bool HOIST>
+template <class F, int NT, int CPL, int FROM, int TO, int AM>
 __device__ __forceinline__ void prime_rows(typename F::W (&A)[CPL], typename F::W (&B)[CPL],
                                            typename F::W (&Cb)[CPL], const uint8_t *w,
                                            uint32_t row, uint32_t nw, uint32_t N, uint32_t stride,
-                                           const LaneState<F, NT, CPL, HOIST> &st)
+                                           const LaneState<F, NT, CPL, AM> &st)
 {
     if constexpr (FROM <= 0 && TO > 0)
         load_row(A, w, row, N, stride, st);
@@ -259,21 +289,25 @@ __device__ __forceinline__ void prime_rows(typename F::W (&A)[CPL], typename F::
 // row DEPTH - 1 ahead, then reduces the oldest (the loads of a step always come
 // first in the loop body: with the reduction first, the compiler waits for every
 // load at the loop head).
-template <class F, int NT, int CPL, int DEPTH, bool HOIST>
+template <class F, int NT, int CPL, int DEPTH, int AM>
 __device__ __forceinline__ void stream_rows(typename F::W (&A)[CPL], typename F::W (&B)[CPL],
                                             typename F::W (&Cb)[CPL], const uint8_t *w,
                                             uint32_t row, uint32_t nw, uint32_t N,
                                             uint32_t stride,
-                                            const LaneState<F, NT, CPL, HOIST> &st,
+                                            const LaneState<F, NT, CPL, AM> &st,
                                             const int8_t *qs, const uint16_t *d8, uint32_t K,
                                             float *y, uint32_t ldy, uint32_t lane)
 {
     // look-ahead rows past the end get an empty descriptor (load_row), so every load
     // stays unconditional and their results are never reduced
-#define Q6K_FINISH(BUF, ROW) finish_row<F, NT, CPL, HOIST>(BUF, st, qs, d8, K, y, ldy, ROW, lane)
+#define Q6K_FINISH(BUF, ROW) finish_row<F, NT, CPL, AM>(BUF, st, qs, d8, K, y, ldy, ROW, lane)
     if constexpr (DEPTH == 1) {
         for (; row < N; row += nw) {
+            // all of the row's loads before any of its arithmetic (without the
+            // barrier the compiler interleaves them, waiting for one group of loads
+            // before it issues the next)
             load_row(A, w, row, N, stride, st);
+            __builtin_amdgcn_sched_barrier(0);
             Q6K_FINISH(A, row);
         }
     } else if constexpr (DEPTH == 2) {
@@ -317,13 +351,13 @@ __device__ __forceinline__ void stream_rows(typename F::W (&A)[CPL], typename F:
 
 // The same walk with all DEPTH first rows already requested: one step of the
 // walk peeled off without its first request, then stream_rows from the next row.
-template <class F, int NT, int CPL, int DEPTH, bool HOIST>
+template <class F, int NT, int CPL, int DEPTH, int AM>
 __device__ __forceinline__ void stream_rows_primed(typename F::W (&A)[CPL],
                                                    typename F::W (&B)[CPL],
                                                    typename F::W (&Cb)[CPL], const uint8_t *w,
                                                    uint32_t row, uint32_t nw, uint32_t N,
                                                    uint32_t stride,
-                                                   const LaneState<F, NT, CPL, HOIST> &st,
+                                                   const LaneState<F, NT, CPL, AM> &st,
                                                    const int8_t *qs, const uint16_t *d8,
                                                    uint32_t K, float *y, uint32_t ldy,
                                                    uint32_t lane)
@@ -333,7 +367,7 @@ __device__ __forceinline__ void stream_rows_primed(typename F::W (&A)[CPL],
     if (r1 >= N)
         return;
     if constexpr (DEPTH == 1) {
-        stream_rows<F, NT, CPL, DEPTH, HOIST>(A, B, Cb, w, r1, nw, N, stride, st, qs, d8, K, y,
+        stream_rows<F, NT, CPL, DEPTH, AM>(A, B, Cb, w, r1, nw, N, stride, st, qs, d8, K, y,
                                               ldy, lane);
     } else if constexpr (DEPTH == 2) {
         load_row(A, w, r2, N, stride, st);
@@ -341,7 +375,7 @@ __device__ __forceinline__ void stream_rows_primed(typename F::W (&A)[CPL],
         Q6K_FINISH(B, r1);
         if (r2 >= N)
             return;
-        stream_rows<F, NT, CPL, DEPTH, HOIST>(A, B, Cb, w, r2, nw, N, stride, st, qs, d8, K, y,
+        stream_rows<F, NT, CPL, DEPTH, AM>(A, B, Cb, w, r2, nw, N, stride, st, qs, d8, K, y,
                                               ldy, lane);
     } else {
         load_row(A, w, r3, N, stride, st);
@@ -354,14 +388,41 @@ __device__ __forceinline__ void stream_rows_primed(typename F::W (&A)[CPL],
         Q6K_FINISH(Cb, r2);
         if (r3 >= N)
             return;
-        stream_rows<F, NT, CPL, DEPTH, HOIST>(A, B, Cb, w, r3, nw, N, stride, st, qs, d8, K, y,
+        stream_rows<F, NT, CPL, DEPTH, AM>(A, B, Cb, w, r3, nw, N, stride, st, qs, d8, K, y,
                                               ldy, lane);
     }
 }
 #undef Q6K_FINISH
 
+// Bytes of LDS the ACT_LDS kernels stage for NT tokens of C chunks: three planes of
+// NT * (C + 1) 16-byte entries (each token's chunks, then its all-zero entry).
+constexpr uint32_t act_lds_bytes(int nt, uint32_t C)
+{
+    return 3u * 16u * (uint32_t)nt * (C + 1u);
+}
+
+// ACT_LDS staging, by every thread of the workgroup: the operands of token t, chunk Q
+// (first halves, second halves, scalars) at entry t * (C + 1) + Q of each plane, and
+// zeros at entry t * (C + 1) + C. Ends with a barrier.
+template <class F, int NT>
+__device__ __forceinline__ void stage_acts(uint4 *lds, const int8_t *qs, const uint16_t *d8,
+                                           uint32_t K, uint32_t C)
+{
+    const uint32_t per = C + 1u, plane = (uint32_t)NT * per;
+    for (uint32_t e = threadIdx.x; e < plane; e += WG) {
+        const uint32_t t = e / per, Q = e - t * per;
+        uint4 xa = make_uint4(0u, 0u, 0u, 0u), xb = xa, sc = xa;
+        if (Q < C)
+            F::to_words(F::act(qs + (size_t)t * K, d8 + (size_t)t * (K / 32), Q), xa, xb, sc);
+        lds[e] = xa;
+        lds[plane + e] = xb;
+        lds[2u * plane + e] = sc;
+    }
+    __syncthreads();
+}
+
 // Rows with at most MAX_CPL chunks per lane; DEPTH rows in flight per wave.
-template <class F, int NT, int CPL, int DEPTH, bool HOIST>
+template <class F, int NT, int CPL, int DEPTH, int AM>
 __global__ __launch_bounds__(WG) void mmvq_rows(const uint8_t *__restrict__ w,
                                                 const int8_t *__restrict__ qs,
                                                 const uint16_t *__restrict__ d8,
@@ -371,14 +432,33 @@ __global__ __launch_bounds__(WG) void mmvq_rows(const uint8_t *__restrict__ w,
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = blockIdx.x * WAVES_PER_WG + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t nw = gridDim.x * WAVES_PER_WG;
-    LaneState<F, NT, CPL, HOIST> st;
-    lane_init(st, lane, nbe, qs, d8, K);
-    if (wave >= N)
-        return;
+    LaneState<F, NT, CPL, AM> st;
     typename F::W A[CPL], B[CPL], Cb[CPL];
-    prime_rows<F, NT, CPL, 0, DEPTH - 1, HOIST>(A, B, Cb, w, wave, nw, N, stride, st);
-    stream_rows<F, NT, CPL, DEPTH, HOIST>(A, B, Cb, w, wave, nw, N, stride, st, qs, d8, K, y,
-                                          ldy, lane);
+    if constexpr (AM == ACT_LDS) {
+        extern __shared__ uint4 s_act[];
+        const uint32_t C = 8u * nbe;
+        lane_chunks(st, lane, nbe);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+            st.ent[i] = st.live[i] ? st.Q[i] : C;
+        st.lds = s_act;
+        st.tstride = C + 1u;
+        st.plane = (uint32_t)NT * (C + 1u);
+        // the first rows' weights are requested before the staging (a wave with no row
+        // primes empty descriptors), so the weight stream is under way meanwhile
+        prime_rows<F, NT, CPL, 0, DEPTH - 1, AM>(A, B, Cb, w, wave, nw, N, stride, st);
+        __builtin_amdgcn_sched_barrier(0);
+        stage_acts<F, NT>(s_act, qs, d8, K, C);
+        if (wave >= N)
+            return;
+    } else {
+        lane_init(st, lane, nbe, qs, d8, K);
+        if (wave >= N)
+            return;
+        prime_rows<F, NT, CPL, 0, DEPTH - 1, AM>(A, B, Cb, w, wave, nw, N, stride, st);
+    }
+    stream_rows<F, NT, CPL, DEPTH, AM>(A, B, Cb, w, wave, nw, N, stride, st, qs, d8, K, y,
+                                       ldy, lane);
 }
 
 // RMSNorm -> q8 -> GEMV in one kernel, for the shapes whose activation operands
@@ -435,12 +515,12 @@ __global__ __launch_bounds__(WG) void mmvq_rmsnorm_rows(
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    LaneState<F, NT, CPL, true> st;
+    LaneState<F, NT, CPL, ACT_REGS> st;
     lane_chunks(st, lane, nbe);
     typename F::W A[CPL], B[CPL], Cb[CPL];
     // a wave with no row primes empty descriptors (no memory traffic); it still
     // takes part in the workgroup's norm below
-    prime_rows<F, NT, CPL, 0, PRE, true>(A, B, Cb, w, wave, nw, N, stride, st);
+    prime_rows<F, NT, CPL, 0, PRE, ACT_REGS>(A, B, Cb, w, wave, nw, N, stride, st);
     __builtin_amdgcn_sched_barrier(0);
 
     const bool store = blockIdx.x == 0;
@@ -463,9 +543,9 @@ __global__ __launch_bounds__(WG) void mmvq_rmsnorm_rows(
     lane_acts(st, reinterpret_cast<const int8_t *>(&s_qs[0][0]), &s_d8[0][0], 4u * K4_MAX);
     if (wave >= N)
         return;
-    prime_rows<F, NT, CPL, PRE, DEPTH, true>(A, B, Cb, w, wave, nw, N, stride, st);
+    prime_rows<F, NT, CPL, PRE, DEPTH, ACT_REGS>(A, B, Cb, w, wave, nw, N, stride, st);
     __builtin_amdgcn_sched_barrier(0);
-    stream_rows_primed<F, NT, CPL, DEPTH, true>(A, B, Cb, w, wave, nw, N, stride, st, nullptr,
+    stream_rows_primed<F, NT, CPL, DEPTH, ACT_REGS>(A, B, Cb, w, wave, nw, N, stride, st, nullptr,
                                                 nullptr, K, y, ldy, lane);
 }
 
@@ -491,7 +571,7 @@ __global__ __launch_bounds__(WG) void gate_up_swiglu_rows(
     __shared__ float s_g[32], s_u[32];
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    LaneState<F, 1, CPL, true> st;
+    LaneState<F, 1, CPL, ACT_REGS> st;
     lane_init(st, lane, nbe, qs, d8, K);
     const uint32_t N = 2u * Nh, nblk = Nh / 32u;
     typename F::W A[CPL], B[CPL];
@@ -509,12 +589,12 @@ __global__ __launch_bounds__(WG) void gate_up_swiglu_rows(
         for (uint32_t i = 0; i < ROWS; i += 2) {
             load_row(B, w, row_of(i + 1), N, stride, st);
             __builtin_amdgcn_sched_barrier(0);
-            take(i, row_total<F, 1, CPL, true>(A, st, nullptr, nullptr, K, lane));
+            take(i, row_total<F, 1, CPL, ACT_REGS>(A, st, nullptr, nullptr, K, lane));
             if (i + 2 < ROWS) {
                 load_row(A, w, row_of(i + 2), N, stride, st);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            take(i + 1, row_total<F, 1, CPL, true>(B, st, nullptr, nullptr, K, lane));
+            take(i + 1, row_total<F, 1, CPL, ACT_REGS>(B, st, nullptr, nullptr, K, lane));
         }
         __syncthreads();
         if (wv == 0) {
@@ -575,6 +655,7 @@ __global__ __launch_bounds__(WG) void mmvq_long(const uint8_t *__restrict__ w,
                 Qs[i] = live[i] ? Q : C - 1u;
                 wt[i] = F::load(r, F::offsets(Qs[i], nbe));
             }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < STEP; ++i) {
 #pragma unroll
@@ -682,7 +763,7 @@ namespace {
 // register-budget rule: depth 2 in registers while nt * chunks <= 6, else depth 1.
 struct RowsCfg {
     int depth;
-    bool hoist;
+    int mode;       // ActMode
     int wg_per_cu;
 };
 
@@ -691,48 +772,41 @@ constexpr RowsCfg rows_cfg(int type, int nt, int cpl)
     const bool q6 = type == KQT_Q6_K, q4 = type == KQT_Q4_K;
     if (nt == 1) {
         if (cpl == 1)
-            return {2, true, 4};
+            return {2, ACT_REGS, 4};
         if (cpl == 2)
-            return {2, true, 2};
+            return {2, ACT_REGS, 2};
         if (cpl == 3)
-            return q6 ? RowsCfg{3, true, 1} : RowsCfg{2, true, 2};
-        if (cpl <= 6 || (cpl == 7 && q4) || (cpl == 11 && q6))
-            return {2, true, 1};
-        return {1, true, 2};
+            return q6 ? RowsCfg{3, ACT_REGS, 1} : RowsCfg{2, ACT_REGS, 2};
+        if (cpl <= 6)
+            return {2, ACT_REGS, 1};
+        // long rows: q4_K/q5_K operands (and q6_K's from 11 chunks) staged in LDS
+        // leave registers for two workgroups per CU
+        if (!q6 || cpl >= 11)
+            return {1, ACT_LDS, 2};
+        return {1, ACT_REGS, cpl <= 8 ? 1 : 2};
     }
     if (cpl == 1)
-        return {3, true, 2};
+        return {3, ACT_REGS, 2};
     if (cpl == 2)
-        return (nt == 2 && !q6) ? RowsCfg{3, true, 2} : RowsCfg{2, true, 2};
+        return (nt == 2 && !q6) ? RowsCfg{3, ACT_REGS, 2} : RowsCfg{2, ACT_REGS, 2};
     if (cpl == 4 && nt == 2 && q6)
-        return {2, true, 1};
+        return {2, ACT_REGS, 1};
+    // long rows at several tokens: the columns' operands no longer fit in registers
+    // next to the weight buffers, and staging them in LDS (read per row) measured
+    // faster than registers, than re-reading them from the plane, and than one or
+    // two columns per launch (q6_K 4096x24576 at 4 columns: 60 us in two launches of
+    // two, 34 us with LDS); q4_K and q5_K carry more operand registers per chunk and
+    // cross over earlier
+    const bool lds = q6 ? (cpl >= 11 || (cpl >= 8 && nt >= 3))
+                        : q4 ? (cpl >= 7 || (cpl == 6 && nt >= 3))
+                             : (cpl >= 9 || (cpl >= 7 && nt >= 3) || (cpl == 6 && nt == 4));
+    if (lds)
+        return {2, ACT_LDS, 2};
     if (cpl <= 6)
-        return {2, true, 2};
-    // 7 or more chunks per lane: at most two tokens per launch (tokens_per_launch),
-    // except q6_K and q4_K at 7
-    if (nt == 2) {
-        if (q6)
-            return cpl == 7 ? RowsCfg{2, true, 1} : RowsCfg{1, true, 2};
-        return (q4 || cpl <= 10) ? RowsCfg{2, true, 1} : RowsCfg{1, true, 2};
-    }
-    return q6 ? RowsCfg{1, true, 2} : RowsCfg{2, true, 1};
-}
-
-// Token columns per launch: each launch reads the weights once for its columns, but
-// every column's activation operands live in registers across the whole row, and
-// past six chunks per lane four columns no longer fit them. There one or two columns
-// per launch, reading the weights two or four times, measured faster than the
-// four-column kernels (graph-replayed sweeps of 4096-row matrices, 7..12 chunks per
-// lane: e.g. q6_K at 10 chunks 60 us for four columns in one launch, 33 us in two).
-constexpr int tokens_per_launch(int type, int cpl)
-{
-    if (cpl <= 6)
-        return MAX_NT_KERNEL;
-    if (type == KQT_Q6_K)
-        return cpl == 7 ? 4 : 2;
-    if (type == KQT_Q4_K)
-        return cpl == 7 ? 4 : (cpl <= 10 ? 2 : 1);
-    return cpl <= 8 ? 2 : 1;
+        return {2, ACT_REGS, 2};
+    if (nt == 2)
+        return (q6 && cpl >= 8) ? RowsCfg{1, ACT_REGS, 2} : RowsCfg{2, ACT_REGS, 1};
+    return {1, ACT_REGS, 2};
 }
 
 struct GemvArgs {
@@ -747,18 +821,25 @@ struct GemvArgs {
 // runtime's occupancy calculator, cached per kernel. Some long-row kernels need more
 // than the 256 registers per lane that two workgroups per CU leave; a grid sized
 // for two would then run in two rounds.
-int wg_fit(const void *kern)
+// lds: the launch's dynamic LDS bytes (the kernel's own static LDS is known to the
+// runtime); past 64 KB the kernel is first allowed that much.
+int wg_fit(const void *kern, uint32_t lds = 0)
 {
     static std::mutex mu;
-    static std::unordered_map<const void *, int> cache;
+    static std::map<std::pair<const void *, uint32_t>, int> cache;
     std::lock_guard<std::mutex> lock(mu);
-    auto it = cache.find(kern);
+    const auto key = std::make_pair(kern, lds);
+    auto it = cache.find(key);
     if (it != cache.end())
         return it->second;
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, WG, 0) != hipSuccess || n < 1)
+    if (lds > 65536u &&
+        hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
+            hipSuccess)
         return 0;
-    cache.emplace(kern, n);
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, WG, lds) != hipSuccess || n < 1)
+        return 0;
+    cache.emplace(key, n);
     return n;
 }
 
@@ -772,15 +853,16 @@ uint32_t grid_for(int64_t N, int num_cu, int wg_per_cu)
 }
 
 template <typename Kern>
-hipError_t launch(Kern kern, int num_cu, int wg_per_cu, hipStream_t s, GemvArgs a)
+hipError_t launch(Kern kern, int num_cu, int wg_per_cu, hipStream_t s, GemvArgs a,
+                  uint32_t lds = 0)
 {
-    const int fit = wg_fit((const void *)kern);
+    const int fit = wg_fit((const void *)kern, lds);
     if (fit < 1)
         return hipErrorInvalidValue;
     const uint32_t grid = grid_for(a.N, num_cu, wg_per_cu < fit ? wg_per_cu : fit);
     void *args[] = {(void *)&a.w, (void *)&a.qs, (void *)&a.d8, (void *)&a.y, (void *)&a.N,
                     (void *)&a.nbe, (void *)&a.stride, (void *)&a.K, (void *)&a.ldy};
-    return hipLaunchKernel((const void *)kern, dim3(grid), dim3(WG), args, 0, s);
+    return hipLaunchKernel((const void *)kern, dim3(grid), dim3(WG), args, lds, s);
 }
 
 template <class F, int NT, int CPL>
@@ -789,11 +871,10 @@ hipError_t launch_cpl(const RowsCfg &c, int num_cu, hipStream_t s, const GemvArg
     // the one (depth, hoist) pair rows_cfg picks for this type, NT and CPL is built,
     // for the token counts a launch of this CPL can have
     constexpr RowsCfg k = rows_cfg(F::TYPE, NT, CPL);
-    if constexpr (NT <= tokens_per_launch(F::TYPE, CPL)) {
-        if (c.depth == k.depth && c.hoist == k.hoist)
-            return launch(mmvq_rows<F, NT, CPL, k.depth, k.hoist>, num_cu, c.wg_per_cu, s, a);
-    }
-    return hipErrorInvalidValue;
+    if (c.depth != k.depth || c.mode != k.mode)
+        return hipErrorInvalidValue;
+    const uint32_t lds = k.mode == ACT_LDS ? act_lds_bytes(NT, 8u * a.nbe) : 0u;
+    return launch(mmvq_rows<F, NT, CPL, k.depth, k.mode>, num_cu, c.wg_per_cu, s, a, lds);
 }
 
 template <class F, int NT, int... CPLS>
@@ -850,7 +931,7 @@ hipError_t launch_fused_cpl(int depth, int num_cu, int wg_per_cu, hipStream_t s,
                         (void *)&a.ldy};
         // the depth rows_cfg picks for this type, NT and CPL (always in registers here)
         constexpr RowsCfg k = rows_cfg(F::TYPE, NT, CPL);
-        static_assert(k.hoist, "the fused kernel keeps the activation in registers");
+        static_assert(k.mode == ACT_REGS, "the fused kernel keeps the activation in registers");
         const void *kern = depth == k.depth ? (const void *)mmvq_rmsnorm_rows<F, NT, CPL, k.depth>
                                             : nullptr;
         const int fit = kern ? wg_fit(kern) : 0;
@@ -882,9 +963,8 @@ hipError_t launch_mmvq_fmt(const uint8_t *w, const uint8_t *q8, float *y, int64_
     const int8_t *qs = reinterpret_cast<const int8_t *>(q8);
     const uint16_t *d8 = reinterpret_cast<const uint16_t *>(q8 + (size_t)nt * K);
     const int cpl = (int)((8u * nbe + 63u) / 64u);
-    const int step = cpl <= MAX_CPL ? tokens_per_launch(F::TYPE, cpl) : MAX_NT_KERNEL;
-    for (int t0 = 0; t0 < nt; t0 += step) {
-        const int n = nt - t0 < step ? nt - t0 : step;
+    for (int t0 = 0; t0 < nt; t0 += MAX_NT_KERNEL) {
+        const int n = nt - t0 < MAX_NT_KERNEL ? nt - t0 : MAX_NT_KERNEL;
         GemvArgs a;
         a.w = w;
         a.qs = qs + (size_t)t0 * K;
@@ -1002,11 +1082,10 @@ MmvqPlan plan_mmvq(int type, int64_t N, int64_t K, int nt, int num_cu)
     const int64_t nbe = K / 256;
     p.cpl = (int)((8 * nbe + 63) / 64);
     p.unrolled = p.cpl <= MAX_CPL;
-    const int step = p.unrolled ? tokens_per_launch(type, p.cpl) : MAX_NT_KERNEL;
-    p.launches = (nt + step - 1) / step;
-    const int nt0 = nt < step ? nt : step;
-    const RowsCfg c = p.unrolled ? rows_cfg(type, nt0, p.cpl) : RowsCfg{1, false, 2};
-    p.hoist = p.unrolled && c.hoist;
+    p.launches = (nt + MAX_NT_KERNEL - 1) / MAX_NT_KERNEL;
+    const int nt0 = nt < MAX_NT_KERNEL ? nt : MAX_NT_KERNEL;
+    const RowsCfg c = p.unrolled ? rows_cfg(type, nt0, p.cpl) : RowsCfg{1, ACT_GLOBAL, 2};
+    p.act_mode = c.mode;
     p.depth = c.depth;
     p.grid = grid_for(N, num_cu, c.wg_per_cu);
     return p;

@@ -14,8 +14,9 @@ struct MmvqPlan {
     uint32_t grid = 0;      // workgroups of 256 threads (before the occupancy clamp)
     int cpl = 0;            // low-bit chunks per lane per row
     bool unrolled = false;  // a fixed-CPL kernel (else the generic stepping kernel)
-    bool hoist = false;     // activation operands held in registers across rows
-    int launches = 0;       // one launch per group of token columns (up to 4)
+    int act_mode = 0;       // activation operands across rows: 0 re-read per row,
+                            // 1 registers, 2 staged in LDS once per workgroup
+    int launches = 0;       // one launch per group of up to 4 token columns
     int depth = 1;          // rows in flight per wave
 };
 

@@ -226,6 +226,28 @@ struct FmtQ6K {
         a.da = 0.0f;
         a.db = 0.0f;
     }
+
+    // The operands as three 16-byte words (LDS staging) and back; all-zero words give
+    // operands that contribute exactly zero.
+    __device__ static void to_words(const Act &a, uint4 &xa, uint4 &xb, uint4 &sc)
+    {
+        xa = a.xa;
+        xb = a.xb;
+        sc = make_uint4(__builtin_bit_cast(uint32_t, a.da), __builtin_bit_cast(uint32_t, a.db),
+                        (uint32_t)a.na, (uint32_t)a.nb);
+    }
+    __device__ static Act from_words(const uint4 &xa, const uint4 &xb, const uint4 &sc)
+    {
+        const uint32_t s0 = sc.x, s1 = sc.y, s2 = sc.z, s3 = sc.w;
+        Act a;
+        a.xa = xa;
+        a.xb = xb;
+        a.da = __builtin_bit_cast(float, s0);
+        a.db = __builtin_bit_cast(float, s1);
+        a.na = (int)s2;
+        a.nb = (int)s3;
+        return a;
+    }
 };
 
 }  // namespace q6k
