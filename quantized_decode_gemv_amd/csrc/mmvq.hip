@@ -268,60 +268,68 @@ __device__ __forceinline__ void finish_row(const typename F::W (&src)[CPL],
         y[(size_t)t * ldy + row] = s;
 }
 
+// The weight buffers of the rows a wave has in flight (up to three; a kernel's
+// unused ones are never touched and cost nothing). A fourth row in flight measured
+// slower on lm_head-shaped rows (GEMV 91.2 vs 90.8 us, fused 93.6 vs 93.0 us).
+template <class F, int CPL>
+struct RowBufs {
+    typename F::W A[CPL], B[CPL], C[CPL];
+};
+
 // Requests rows FROM .. TO - 1 of a wave's walk (row, row + nw, ...), the first
-// DEPTH of which go to A, B and Cb in that order.
+// DEPTH of which go to A, B and C in that order.
 template <class F, int NT, int CPL, int FROM, int TO, int AM>
-__device__ __forceinline__ void prime_rows(typename F::W (&A)[CPL], typename F::W (&B)[CPL],
-                                           typename F::W (&Cb)[CPL], const uint8_t *w,
-                                           uint32_t row, uint32_t nw, uint32_t N, uint32_t stride,
+__device__ __forceinline__ void prime_rows(RowBufs<F, CPL> &b, const uint8_t *w, uint32_t row,
+                                           uint32_t nw, uint32_t N, uint32_t stride,
                                            const LaneState<F, NT, CPL, AM> &st)
 {
     if constexpr (FROM <= 0 && TO > 0)
-        load_row(A, w, row, N, stride, st);
+        load_row(b.A, w, row, N, stride, st);
     if constexpr (FROM <= 1 && TO > 1)
-        load_row(B, w, row + nw, N, stride, st);
+        load_row(b.B, w, row + nw, N, stride, st);
     if constexpr (FROM <= 2 && TO > 2)
-        load_row(Cb, w, row + 2u * nw, N, stride, st);
+        load_row(b.C, w, row + 2u * nw, N, stride, st);
 }
 
+// One step of a walk: request row `next` into buffer NB, then reduce row `row` held
+// in buffer CB (the request comes first: with the reduction first, the compiler
+// waits for every load at the loop head; the scheduling barrier keeps it from
+// sinking the loads below the arithmetic).
+#define Q6K_STEP(NB, NEXT, CB, ROW)                                                            \
+    do {                                                                                        \
+        load_row(b.NB, w, NEXT, N, stride, st);                                                 \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        finish_row<F, NT, CPL, AM>(b.CB, st, qs, d8, K, y, ldy, ROW, lane);                     \
+    } while (0)
+
 // A wave's walk over rows row, row + nw, ... < N with DEPTH rows in flight, the
-// first DEPTH - 1 of them already requested by prime_rows. Each step requests the
-// row DEPTH - 1 ahead, then reduces the oldest (the loads of a step always come
-// first in the loop body: with the reduction first, the compiler waits for every
-// load at the loop head).
+// first DEPTH - 1 of them already requested by prime_rows. Look-ahead rows past the
+// end get an empty descriptor (load_row), so every load stays unconditional and
+// their results are never reduced.
 template <class F, int NT, int CPL, int DEPTH, int AM>
-__device__ __forceinline__ void stream_rows(typename F::W (&A)[CPL], typename F::W (&B)[CPL],
-                                            typename F::W (&Cb)[CPL], const uint8_t *w,
-                                            uint32_t row, uint32_t nw, uint32_t N,
-                                            uint32_t stride,
+__device__ __forceinline__ void stream_rows(RowBufs<F, CPL> &b, const uint8_t *w, uint32_t row,
+                                            uint32_t nw, uint32_t N, uint32_t stride,
                                             const LaneState<F, NT, CPL, AM> &st,
                                             const int8_t *qs, const uint16_t *d8, uint32_t K,
                                             float *y, uint32_t ldy, uint32_t lane)
 {
-    // look-ahead rows past the end get an empty descriptor (load_row), so every load
-    // stays unconditional and their results are never reduced
-#define Q6K_FINISH(BUF, ROW) finish_row<F, NT, CPL, AM>(BUF, st, qs, d8, K, y, ldy, ROW, lane)
+    static_assert(DEPTH >= 1 && DEPTH <= 3, "one to three rows in flight");
     if constexpr (DEPTH == 1) {
+        // all of the row's loads before any of its arithmetic (without the barrier
+        // the compiler interleaves them, waiting for one group of loads before it
+        // issues the next)
         for (; row < N; row += nw) {
-            // all of the row's loads before any of its arithmetic (without the
-            // barrier the compiler interleaves them, waiting for one group of loads
-            // before it issues the next)
-            load_row(A, w, row, N, stride, st);
+            load_row(b.A, w, row, N, stride, st);
             __builtin_amdgcn_sched_barrier(0);
-            Q6K_FINISH(A, row);
+            finish_row<F, NT, CPL, AM>(b.A, st, qs, d8, K, y, ldy, row, lane);
         }
     } else if constexpr (DEPTH == 2) {
         for (;;) {
-            const uint32_t r1 = row + nw;
-            load_row(B, w, r1, N, stride, st);
-            __builtin_amdgcn_sched_barrier(0);
-            Q6K_FINISH(A, row);
+            const uint32_t r1 = row + nw, r2 = r1 + nw;
+            Q6K_STEP(B, r1, A, row);
             if (r1 >= N)
                 break;
-            const uint32_t r2 = r1 + nw;
-            load_row(A, w, r2, N, stride, st);
-            __builtin_amdgcn_sched_barrier(0);
-            Q6K_FINISH(B, r1);
+            Q6K_STEP(A, r2, B, r1);
             if (r2 >= N)
                 break;
             row = r2;
@@ -329,19 +337,13 @@ __device__ __forceinline__ void stream_rows(typename F::W (&A)[CPL], typename F:
     } else {
         for (;;) {
             const uint32_t r1 = row + nw, r2 = r1 + nw, r3 = r2 + nw;
-            load_row(Cb, w, r2, N, stride, st);
-            __builtin_amdgcn_sched_barrier(0);
-            Q6K_FINISH(A, row);
+            Q6K_STEP(C, r2, A, row);
             if (r1 >= N)
                 break;
-            load_row(A, w, r3, N, stride, st);
-            __builtin_amdgcn_sched_barrier(0);
-            Q6K_FINISH(B, r1);
+            Q6K_STEP(A, r3, B, r1);
             if (r2 >= N)
                 break;
-            load_row(B, w, r3 + nw, N, stride, st);
-            __builtin_amdgcn_sched_barrier(0);
-            Q6K_FINISH(Cb, r2);
+            Q6K_STEP(B, r3 + nw, C, r2);
             if (r3 >= N)
                 break;
             row = r3;
@@ -349,12 +351,11 @@ __device__ __forceinline__ void stream_rows(typename F::W (&A)[CPL], typename F:
     }
 }
 
-// The same walk with all DEPTH first rows already requested: one step of the
-// walk peeled off without its first request, then stream_rows from the next row.
+// The same walk with all DEPTH first rows already requested: the walk's first
+// DEPTH - 1 steps peeled off (the first without its request), then stream_rows from
+// the row DEPTH - 1 further on, whose DEPTH - 1 rows are then in flight.
 template <class F, int NT, int CPL, int DEPTH, int AM>
-__device__ __forceinline__ void stream_rows_primed(typename F::W (&A)[CPL],
-                                                   typename F::W (&B)[CPL],
-                                                   typename F::W (&Cb)[CPL], const uint8_t *w,
+__device__ __forceinline__ void stream_rows_primed(RowBufs<F, CPL> &b, const uint8_t *w,
                                                    uint32_t row, uint32_t nw, uint32_t N,
                                                    uint32_t stride,
                                                    const LaneState<F, NT, CPL, AM> &st,
@@ -363,36 +364,27 @@ __device__ __forceinline__ void stream_rows_primed(typename F::W (&A)[CPL],
                                                    uint32_t lane)
 {
     const uint32_t r1 = row + nw, r2 = r1 + nw, r3 = r2 + nw;
-    Q6K_FINISH(A, row);
+    finish_row<F, NT, CPL, AM>(b.A, st, qs, d8, K, y, ldy, row, lane);
     if (r1 >= N)
         return;
     if constexpr (DEPTH == 1) {
-        stream_rows<F, NT, CPL, DEPTH, AM>(A, B, Cb, w, r1, nw, N, stride, st, qs, d8, K, y,
-                                              ldy, lane);
+        stream_rows<F, NT, CPL, DEPTH, AM>(b, w, r1, nw, N, stride, st, qs, d8, K, y, ldy, lane);
     } else if constexpr (DEPTH == 2) {
-        load_row(A, w, r2, N, stride, st);
-        __builtin_amdgcn_sched_barrier(0);
-        Q6K_FINISH(B, r1);
+        Q6K_STEP(A, r2, B, r1);
         if (r2 >= N)
             return;
-        stream_rows<F, NT, CPL, DEPTH, AM>(A, B, Cb, w, r2, nw, N, stride, st, qs, d8, K, y,
-                                              ldy, lane);
+        stream_rows<F, NT, CPL, DEPTH, AM>(b, w, r2, nw, N, stride, st, qs, d8, K, y, ldy, lane);
     } else {
-        load_row(A, w, r3, N, stride, st);
-        __builtin_amdgcn_sched_barrier(0);
-        Q6K_FINISH(B, r1);
+        Q6K_STEP(A, r3, B, r1);
         if (r2 >= N)
             return;
-        load_row(B, w, r3 + nw, N, stride, st);
-        __builtin_amdgcn_sched_barrier(0);
-        Q6K_FINISH(Cb, r2);
+        Q6K_STEP(B, r3 + nw, C, r2);
         if (r3 >= N)
             return;
-        stream_rows<F, NT, CPL, DEPTH, AM>(A, B, Cb, w, r3, nw, N, stride, st, qs, d8, K, y,
-                                              ldy, lane);
+        stream_rows<F, NT, CPL, DEPTH, AM>(b, w, r3, nw, N, stride, st, qs, d8, K, y, ldy, lane);
     }
 }
-#undef Q6K_FINISH
+#undef Q6K_STEP
 
 // Bytes of LDS the ACT_LDS kernels stage for NT tokens of C chunks: three planes of
 // NT * (C + 1) 16-byte entries (each token's chunks, then its all-zero entry).
@@ -433,7 +425,7 @@ __global__ __launch_bounds__(WG) void mmvq_rows(const uint8_t *__restrict__ w,
     const uint32_t wave = blockIdx.x * WAVES_PER_WG + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t nw = gridDim.x * WAVES_PER_WG;
     LaneState<F, NT, CPL, AM> st;
-    typename F::W A[CPL], B[CPL], Cb[CPL];
+    RowBufs<F, CPL> bufs;
     if constexpr (AM == ACT_LDS) {
         extern __shared__ uint4 s_act[];
         const uint32_t C = 8u * nbe;
@@ -446,7 +438,7 @@ __global__ __launch_bounds__(WG) void mmvq_rows(const uint8_t *__restrict__ w,
         st.plane = (uint32_t)NT * (C + 1u);
         // the first rows' weights are requested before the staging (a wave with no row
         // primes empty descriptors), so the weight stream is under way meanwhile
-        prime_rows<F, NT, CPL, 0, DEPTH - 1, AM>(A, B, Cb, w, wave, nw, N, stride, st);
+        prime_rows<F, NT, CPL, 0, DEPTH - 1, AM>(bufs, w, wave, nw, N, stride, st);
         __builtin_amdgcn_sched_barrier(0);
         stage_acts<F, NT>(s_act, qs, d8, K, C);
         if (wave >= N)
@@ -455,10 +447,10 @@ __global__ __launch_bounds__(WG) void mmvq_rows(const uint8_t *__restrict__ w,
         lane_init(st, lane, nbe, qs, d8, K);
         if (wave >= N)
             return;
-        prime_rows<F, NT, CPL, 0, DEPTH - 1, AM>(A, B, Cb, w, wave, nw, N, stride, st);
+        prime_rows<F, NT, CPL, 0, DEPTH - 1, AM>(bufs, w, wave, nw, N, stride, st);
     }
-    stream_rows<F, NT, CPL, DEPTH, AM>(A, B, Cb, w, wave, nw, N, stride, st, qs, d8, K, y,
-                                       ldy, lane);
+    stream_rows<F, NT, CPL, DEPTH, AM>(bufs, w, wave, nw, N, stride, st, qs, d8, K, y, ldy,
+                                       lane);
 }
 
 // RMSNorm -> q8 -> GEMV in one kernel, for the shapes whose activation operands
@@ -517,10 +509,10 @@ __global__ __launch_bounds__(WG) void mmvq_rmsnorm_rows(
 
     LaneState<F, NT, CPL, ACT_REGS> st;
     lane_chunks(st, lane, nbe);
-    typename F::W A[CPL], B[CPL], Cb[CPL];
+    RowBufs<F, CPL> bufs;
     // a wave with no row primes empty descriptors (no memory traffic); it still
     // takes part in the workgroup's norm below
-    prime_rows<F, NT, CPL, 0, PRE, ACT_REGS>(A, B, Cb, w, wave, nw, N, stride, st);
+    prime_rows<F, NT, CPL, 0, PRE, ACT_REGS>(bufs, w, wave, nw, N, stride, st);
     __builtin_amdgcn_sched_barrier(0);
 
     const bool store = blockIdx.x == 0;
@@ -543,10 +535,10 @@ __global__ __launch_bounds__(WG) void mmvq_rmsnorm_rows(
     lane_acts(st, reinterpret_cast<const int8_t *>(&s_qs[0][0]), &s_d8[0][0], 4u * K4_MAX);
     if (wave >= N)
         return;
-    prime_rows<F, NT, CPL, PRE, DEPTH, ACT_REGS>(A, B, Cb, w, wave, nw, N, stride, st);
+    prime_rows<F, NT, CPL, PRE, DEPTH, ACT_REGS>(bufs, w, wave, nw, N, stride, st);
     __builtin_amdgcn_sched_barrier(0);
-    stream_rows_primed<F, NT, CPL, DEPTH, ACT_REGS>(A, B, Cb, w, wave, nw, N, stride, st, nullptr,
-                                                nullptr, K, y, ldy, lane);
+    stream_rows_primed<F, NT, CPL, DEPTH, ACT_REGS>(bufs, w, wave, nw, N, stride, st, nullptr,
+                                                    nullptr, K, y, ldy, lane);
 }
 
 // Form B (D4-4 §3.5, the archived fused gate+up+SwiGLU+q8 shape; §5 its closing
