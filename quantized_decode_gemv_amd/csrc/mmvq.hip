@@ -28,7 +28,9 @@
 //    current row's arithmetic (scheduling barriers keep the compiler from sinking
 //    them), so a wave never idles with nothing requested;
 //  - a lane's activation operands are the same for every row; they stay in
-//    registers (HOIST) when they fit, else they are re-read per row (cached);
+//    registers (ACT_REGS) when they fit next to the weight buffers, else the
+//    workgroup stages them once in LDS and reads them per row (ACT_LDS; the
+//    generic long-row kernel re-reads them from the q8 plane);
 //  - a row ends with one reduction for all its token columns (DPP inside each
 //    16-lane row, lane swaps across rows); lanes 0..NT-1 write the NT outputs.
 // The chunks per lane (CPL = ceil(8*nbe/64)) is a template parameter up to
