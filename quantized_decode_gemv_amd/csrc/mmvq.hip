@@ -157,14 +157,16 @@ struct LaneState {
     uint32_t plane, tstride;
 };
 
-template <class F, int NT, int CPL, int AM>
+// A lane's chunks Q = lane + SPAN * i: SPAN = 64 when one wave owns a row, 256 when
+// the four waves of a workgroup share it (lane then counts the workgroup's threads).
+template <class F, int NT, int CPL, int AM, uint32_t SPAN = 64u>
 __device__ __forceinline__ void lane_chunks(LaneState<F, NT, CPL, AM> &st, uint32_t lane,
                                             uint32_t nbe)
 {
     const uint32_t C = 8u * nbe;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-        const uint32_t Q = lane + 64u * i;
+        const uint32_t Q = lane + SPAN * i;
         st.live[i] = Q < C;
         st.Q[i] = st.live[i] ? Q : C - 1u;
         st.off[i] = F::offsets(st.Q[i], nbe);
@@ -453,6 +455,68 @@ __global__ __launch_bounds__(WG) void mmvq_rows(const uint8_t *__restrict__ w,
     }
     stream_rows<F, NT, CPL, DEPTH, AM>(bufs, w, wave, nw, N, stride, st, qs, d8, K, y, ldy,
                                        lane);
+}
+
+// Long rows that are few for the grid: the four waves of a workgroup share each row.
+// Workgroup b owns the R consecutive rows from b * R; every wave walks all of them
+// (DEPTH in flight, the row machine above, one row apart) over its quarter of the
+// chunks (Q = thread + 256 i), reduces its share of a row over its 64 lanes and
+// leaves it in LDS. After the walk one barrier, then each output is the four shares
+// added in a fixed order, (w0 + w1) + (w2 + w3). With one wave per row, a grid of
+// 2048 waves gives such shapes 1.75-2.5 rows per wave: the waves with one row more
+// set the time, and each row's loads wait a whole memory latency. Here every wave has
+// R rows of a quarter the bytes, R is the same for every workgroup but the last, and
+// the chunks per lane fall to what the one-wave rows of lm_head have.
+// LDS: the ACT_LDS operands (if any), then the shares, 4 * NT * R floats.
+template <class F, int NT, int CPL, int DEPTH, int AM>
+__global__ __launch_bounds__(WG) void mmvq_split(const uint8_t *__restrict__ w,
+                                                 const int8_t *__restrict__ qs,
+                                                 const uint16_t *__restrict__ d8,
+                                                 float *__restrict__ y, uint32_t N, uint32_t nbe,
+                                                 uint32_t stride, uint32_t K, uint32_t ldy,
+                                                 uint32_t R)
+{
+    extern __shared__ uint4 s_split[];
+    const uint32_t row0 = blockIdx.x * R;
+    if (row0 >= N)
+        return;   // the whole workgroup: no barrier is reached
+    const uint32_t nr = N - row0 < R ? N - row0 : R;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t C = 8u * nbe;
+    const uint8_t *wb = w + (size_t)row0 * stride;
+    float *part = reinterpret_cast<float *>(
+        s_split + (AM == ACT_LDS ? 3u * (uint32_t)NT * (C + 1u) : 0u));
+    float *share = part + wv * (uint32_t)NT * R;
+    LaneState<F, NT, CPL, AM> st;
+    RowBufs<F, CPL> bufs;
+    lane_chunks<F, NT, CPL, AM, 256u>(st, threadIdx.x, nbe);
+    if constexpr (AM == ACT_LDS) {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+            st.ent[i] = st.live[i] ? st.Q[i] : C;
+        st.lds = s_split;
+        st.tstride = C + 1u;
+        st.plane = (uint32_t)NT * (C + 1u);
+        prime_rows<F, NT, CPL, 0, DEPTH - 1, AM>(bufs, wb, 0u, 1u, nr, stride, st);
+        __builtin_amdgcn_sched_barrier(0);
+        stage_acts<F, NT>(s_split, qs, d8, K, C);
+    } else {
+        if constexpr (AM == ACT_REGS)
+            lane_acts(st, qs, d8, K);
+        prime_rows<F, NT, CPL, 0, DEPTH - 1, AM>(bufs, wb, 0u, 1u, nr, stride, st);
+    }
+    // the shares go where the one-wave kernel stores its outputs: token t of local
+    // row j at share[t * R + j]
+    stream_rows<F, NT, CPL, DEPTH, AM>(bufs, wb, 0u, 1u, nr, stride, st, qs, d8, K, share, R,
+                                       lane);
+    __syncthreads();
+    for (uint32_t e = threadIdx.x; e < (uint32_t)NT * nr; e += WG) {
+        const uint32_t t = e / nr, j = e - t * nr;
+        const float *p = part + t * R + j;
+        const uint32_t ws = (uint32_t)NT * R;
+        y[(size_t)t * ldy + row0 + j] = (p[0] + p[ws]) + (p[2u * ws] + p[3u * ws]);
+    }
 }
 
 // RMSNorm -> q8 -> GEMV in one kernel, for the shapes whose activation operands
@@ -949,6 +1013,91 @@ hipError_t dispatch_fused(int cpl, int depth, std::integer_sequence<int, CPLS...
     return e;
 }
 
+// When the shared-row kernel (mmvq_split) runs a launch of nt <= 4 tokens, from its
+// rows' chunks per lane under one wave per row (cpl), measured against the one-wave
+// kernels (graph-replayed, one MI355X):
+//  - several tokens, cpl >= 7, and cpl = 6 from 3 tokens: every shape measured gains,
+//    most where the one-wave form stages the operands in LDS or runs at depth 1
+//    (q6_K 3584 x 18944 at 4 tokens 28 -> 14 us, 5120 x 13824 19.6 -> 13.4,
+//    16384 x 18944 87 -> 45-49; cpl 6 at 4 tokens 36-39 -> 33); at cpl 5 it loses;
+//  - one token, q4_K / q5_K, cpl >= 7: their one-wave long rows read the operands
+//    from LDS per row; 4-5 % faster (q4_K 5120 x 13824 9.4 -> 9.0 us, 16384 x 24576
+//    38.2 -> 36.3);
+//  - one token, q6_K, cpl >= 7: only when the one-wave grid has fewer than 4 rows per
+//    wave (3584 x 18944 12.5 -> 11.1-11.5 us); with 5 or more it loses 2-4 %
+//    (5120 x 13824, 8192 x 13824, 16384 x 18944).
+// Its chunks per lane are then ceil(cpl / 4) = 2 or 3, its rows per workgroup at most
+// SPLIT_MAX_R (N <= 131072 at two workgroups per CU); longer rows (cpl > MAX_CPL)
+// take the generic stepping kernel.
+constexpr int64_t SPLIT_ROWS_PER_WAVE = 4;
+constexpr uint32_t SPLIT_MAX_R = 256;   // rows per workgroup (LDS: 16 * nt * R bytes)
+
+// Depth, operand mode and workgroups per CU of the shared-row kernel (fitted to the
+// same sweeps: 2 chunks per lane at depth 2 and 2/CU, 3 at depth 3 and 1/CU).
+constexpr RowsCfg split_cfg(int type, int nt, int cpl4)
+{
+    (void)type;
+    (void)nt;
+    return cpl4 <= 2 ? RowsCfg{2, ACT_REGS, 2} : RowsCfg{3, ACT_REGS, 1};
+}
+
+// Rows per workgroup for N rows over num_cu * wg_per_cu workgroups.
+constexpr uint32_t split_rows(int64_t N, int num_cu, int wg_per_cu)
+{
+    const int64_t slots = (int64_t)num_cu * wg_per_cu;
+    return (uint32_t)((N + slots - 1) / slots);
+}
+
+bool split_ok(int type, int nt, int cpl, int64_t N, int num_cu)
+{
+    const int n = nt < MAX_NT_KERNEL ? nt : MAX_NT_KERNEL;
+    if (n < 1 || cpl > MAX_CPL || cpl < 6 || (cpl == 6 && n < 3))
+        return false;
+    if (split_rows(N, num_cu, split_cfg(type, n, (cpl + 3) / 4).wg_per_cu) > SPLIT_MAX_R)
+        return false;
+    if (n > 1 || type != KQT_Q6_K)
+        return true;
+    const int64_t waves = (int64_t)num_cu * rows_cfg(type, n, cpl).wg_per_cu * WAVES_PER_WG;
+    return N < SPLIT_ROWS_PER_WAVE * waves;
+}
+
+template <class F, int NT, int CPL4>
+hipError_t launch_split(int num_cu, hipStream_t s, GemvArgs a)
+{
+    constexpr RowsCfg k = split_cfg(F::TYPE, NT, CPL4);
+    const void *kern = (const void *)mmvq_split<F, NT, CPL4, k.depth, k.mode>;
+    const uint32_t acts = k.mode == ACT_LDS ? act_lds_bytes(NT, 8u * a.nbe) : 0u;
+    int wpc = k.wg_per_cu;
+    uint32_t R = 0, lds = 0;
+    for (;;) {
+        R = split_rows(a.N, num_cu, wpc);
+        if (R > SPLIT_MAX_R)
+            return hipErrorInvalidValue;
+        lds = acts + 16u * (uint32_t)NT * R;
+        const int fit = wg_fit(kern, lds);
+        if (fit < 1)
+            return hipErrorInvalidValue;
+        if (fit >= wpc)
+            break;
+        wpc = fit;
+    }
+    const uint32_t grid = (a.N + R - 1u) / R;
+    void *args[] = {(void *)&a.w, (void *)&a.qs, (void *)&a.d8, (void *)&a.y, (void *)&a.N,
+                    (void *)&a.nbe, (void *)&a.stride, (void *)&a.K, (void *)&a.ldy,
+                    (void *)&R};
+    return hipLaunchKernel(kern, dim3(grid), dim3(WG), args, lds, s);
+}
+
+template <class F, int NT>
+hipError_t dispatch_split(int cpl, int num_cu, hipStream_t s, const GemvArgs &a)
+{
+    switch ((cpl + 3) / 4) {
+    case 2: return launch_split<F, NT, 2>(num_cu, s, a);
+    case 3: return launch_split<F, NT, 3>(num_cu, s, a);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 template <class F>
 hipError_t launch_mmvq_fmt(const uint8_t *w, const uint8_t *q8, float *y, int64_t N, int64_t K,
                            int nt, int num_cu, hipStream_t s)
@@ -970,7 +1119,14 @@ hipError_t launch_mmvq_fmt(const uint8_t *w, const uint8_t *q8, float *y, int64_
         a.K = (uint32_t)K;
         a.ldy = (uint32_t)N;
         hipError_t e;
-        if (cpl <= MAX_CPL) {
+        if (split_ok(F::TYPE, n, cpl, N, num_cu)) {
+            switch (n) {
+            case 1: e = dispatch_split<F, 1>(cpl, num_cu, s, a); break;
+            case 2: e = dispatch_split<F, 2>(cpl, num_cu, s, a); break;
+            case 3: e = dispatch_split<F, 3>(cpl, num_cu, s, a); break;
+            default: e = dispatch_split<F, 4>(cpl, num_cu, s, a); break;
+            }
+        } else if (cpl <= MAX_CPL) {
             const RowsCfg c = rows_cfg(F::TYPE, n, cpl);
             const auto seq = std::make_integer_sequence<int, MAX_CPL>{};
             switch (n) {
@@ -1078,6 +1234,16 @@ MmvqPlan plan_mmvq(int type, int64_t N, int64_t K, int nt, int num_cu)
     p.unrolled = p.cpl <= MAX_CPL;
     p.launches = (nt + MAX_NT_KERNEL - 1) / MAX_NT_KERNEL;
     const int nt0 = nt < MAX_NT_KERNEL ? nt : MAX_NT_KERNEL;
+    if (split_ok(type, nt0, p.cpl, N, num_cu)) {
+        p.shared = true;
+        p.cpl = (p.cpl + 3) / 4;
+        const RowsCfg c = split_cfg(type, nt0, p.cpl);
+        const uint32_t R = split_rows(N, num_cu, c.wg_per_cu);
+        p.act_mode = c.mode;
+        p.depth = c.depth;
+        p.grid = (uint32_t)((N + R - 1) / R);
+        return p;
+    }
     const RowsCfg c = p.unrolled ? rows_cfg(type, nt0, p.cpl) : RowsCfg{1, ACT_GLOBAL, 2};
     p.act_mode = c.mode;
     p.depth = c.depth;

@@ -156,11 +156,39 @@ def test_device_repack_rejects_bad_arguments():
 def test_plan_covers_every_row_length(nbe, nt):
     # every nbe reaches a kernel whose chunk count per lane covers the whole row
     p = q.mmvq_plan(1000, 256 * nbe, nt, 256)
-    assert p["cpl"] * 64 >= 8 * nbe > (p["cpl"] - 1) * 64
-    assert p["unrolled"] == (p["cpl"] <= 12)
+    span = 256 if p["shared"] else 64
+    assert p["cpl"] * span >= 8 * nbe > (p["cpl"] - 1) * span
+    assert p["unrolled"] == (8 * nbe <= 12 * 64)
     assert p["launches"] == -(-nt // 4)
     assert p["act_mode"] in (0, 1, 2)
     assert p["grid"] >= 1 and p["depth"] in (1, 2, 3)
+
+
+@pytest.mark.parametrize("qtype", [14, 12, 13])
+@pytest.mark.parametrize("nbe", [20, 40, 47, 48, 49, 54, 74, 96, 97])
+@pytest.mark.parametrize("N", [1, 3584, 5120, 8192, 131072, 131073, 152064])
+@pytest.mark.parametrize("nt", [1, 2, 3, 4, 5])
+def test_plan_shared_rows_rule(qtype, nbe, N, nt):
+    # the workgroup-shared rows: chunks per lane (one wave per row) 7..12, or 6 from
+    # 3 tokens; at one token q6_K only below 4 rows per wave of the one-wave grid;
+    # at most 256 rows per workgroup
+    cpl = -(-8 * nbe // 64)
+    n = min(nt, 4)
+    p = q.mmvq_plan(N, 256 * nbe, nt, 256, qtype)
+    if not (7 <= cpl <= 12 or (cpl == 6 and n >= 3)):
+        assert not p["shared"]
+        return
+    wpc = 2 if -(-cpl // 4) <= 2 else 1
+    if -(-N // (256 * wpc)) > 256:
+        assert not p["shared"]
+        return
+    if n == 1 and qtype == 14:
+        assert p["shared"] == (N < 4 * 4 * 256 * (2 if cpl >= 9 else 1))
+        if not p["shared"]:
+            return
+    assert p["shared"] and p["cpl"] == -(-cpl // 4)
+    R = -(-N // (256 * wpc))
+    assert p["grid"] == -(-N // R) and p["act_mode"] == 1 and p["depth"] == (2 if wpc == 2 else 3)
 
 
 @pytest.mark.parametrize("N", [1, 2, 3, 63, 64, 65, 1023, 1024, 1025, 4096, 152064])

@@ -99,6 +99,23 @@ def test_dispatch_edges_random(qtype, nbe, nt):
     check_y(y, y_or, A, f"{NAMES[qtype]} nbe={nbe} nt={nt}")
 
 
+@pytest.mark.parametrize("qtype", TYPES, ids=_ids)
+@pytest.mark.parametrize("N,nbe,nt", [(2999, 54, 1), (2999, 74, 4), (1237, 96, 2),
+                                      (2001, 48, 3)])
+def test_shared_rows_random(qtype, N, nbe, nt):
+    # rows shared by the workgroup's four waves: several per workgroup, a short last one
+    K = 256 * nbe
+    p = q.mmvq_plan(N, K, nt, 256, qtype)
+    assert p["shared"]
+    raw = q6ksynth.raw_kq(qtype, N, K, seed=N + nbe * 10 + nt + qtype)
+    dpl = kq_dpl_from_raw(qtype, raw, N, K)
+    x = np.stack([q6ksynth.activation("outlier", K, 1300 + c) for c in range(nt)])
+    qs, d = oracle.quant_q8(x)
+    y = run_kq(qtype, dpl, make_plane(qs, d), N, K, nt)
+    y_or, A = oracle.kq_mmvq(qtype, oracle.RAW, raw, N, K, qs, d, nthreads=oracle_threads())
+    check_y(y, y_or, A, f"{NAMES[qtype]} shared N={N} nbe={nbe} nt={nt}")
+
+
 def _uniform_block(qtype, code, sc, m, d, dmin):
     blk = blank(qtype, 1)[0]
     set_d(qtype, blk, d, dmin)

@@ -106,6 +106,27 @@ def test_dispatch_edges_random(nbe, nt):
     check_y(y, y_or, A, f"nbe={nbe} nt={nt}")
 
 
+# Long rows that the workgroup's four waves share (chunks per lane 7..12, or 6 from 3
+# tokens): several rows per workgroup, a short last workgroup (N not a multiple of
+# the rows per workgroup), both of its chunk counts per thread (2: nbe 49..64, 3:
+# nbe 65..96), one token (q6_K shares them when the rows are few) and several.
+@pytest.mark.parametrize("N,nbe,nt", [(2999, 54, 1), (2999, 54, 2), (2999, 74, 1),
+                                      (2999, 74, 4), (1237, 96, 3), (4097, 49, 5),
+                                      (2001, 48, 3), (3584, 74, 4)])
+def test_shared_rows_random(N, nbe, nt):
+    K = 256 * nbe
+    p = q.mmvq_plan(N, K, nt, 256)
+    say(f"shared rows N={N} nbe={nbe} nt={nt}: plan {p}")
+    assert p["shared"]
+    raw = q6ksynth.raw_q6k(N, K, seed=N + nbe * 10 + nt)
+    dpl = dpl_from_raw(raw, N, K)
+    x = np.stack([q6ksynth.activation("outlier", K, 1200 + c) for c in range(nt)])
+    qs, d = oracle.quant_q8(x)
+    y = run_mmvq(dpl, make_plane(qs, d), N, K, nt)
+    y_or, A = oracle.mmvq(oracle.RAW, raw, N, K, qs, d, nthreads=oracle_threads())
+    check_y(y, y_or, A, f"N={N} nbe={nbe} nt={nt}")
+
+
 @pytest.mark.parametrize("q0", [0, 1, 31, 33, 63])
 @pytest.mark.parametrize("nbe,block", [(1, 0), (4, 3)])
 def test_onehot_diagonal(q0, nbe, block):
