@@ -37,6 +37,8 @@ PAGES_LM_HEAD_GBS = 250.0       # the pages' dpl lm_head content rate (GB10; con
 ROTATE_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mmvq_lm_head_traffic.txt")
 TYPE_NAMES = {12: "q4_K", 13: "q5_K", 14: "q6_K"}
+# the GEMV kernel by the plan's kind
+GEMV_KERNELS = {0: "mmvq_long", 1: "mmvq_rows", 2: "mmvq_split"}
 PRODUCER_NAMES = {"rmsnorm": "fused RMSNorm->q8", "swiglu": "fused SwiGLU->q8",
                   "quant": "q8"}
 KERNEL_SOURCES = [os.path.join(ROOT, "quantized_decode_gemv_amd", "csrc", f)
@@ -345,7 +347,8 @@ def main() -> int:
                    "N": N, "K": K, "nt": nt, "content_bytes": content,
                    "dpl_bytes": dpl_bytes, "weight_copies": copies},
         "dominant_kernel": ("mmvq_rmsnorm_rows (fused)" if fused else
-                            "gate_up_swiglu_rows (Form B)" if formb else "mmvq_rows"),
+                            "gate_up_swiglu_rows (Form B)" if formb else
+                            GEMV_KERNELS[plan["kind"]]),
         "us_per_dominant_kernel": round(kern_us, 2),
         "us_per_gemv": round(gemv_us, 2),
         "ms_per_step_split": round(ms_per_step_split, 5) if ms_per_step_split else None,
