@@ -38,7 +38,7 @@ ROTATE_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mmvq_lm_head_traffic.txt")
 TYPE_NAMES = {12: "q4_K", 13: "q5_K", 14: "q6_K"}
 # the GEMV kernel by the plan's kind
-GEMV_KERNELS = {0: "mmvq_long", 1: "mmvq_rows", 2: "mmvq_split"}
+GEMV_KERNELS = {0: "mmvq_long", 1: "mmvq_rows", 2: "mmvq_split", 3: "mmvq_pairs"}
 PRODUCER_NAMES = {"rmsnorm": "fused RMSNorm->q8", "swiglu": "fused SwiGLU->q8",
                   "quant": "q8"}
 KERNEL_SOURCES = [os.path.join(ROOT, "quantized_decode_gemv_amd", "csrc", f)

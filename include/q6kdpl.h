@@ -246,16 +246,23 @@ int mmvq_kq_q8_subdots(int type, const void *w_dpl, const void *q8, int32_t *dot
 
 /* Diagnostics: how mmvq_q6k_q8 runs a shape on a device with num_cu compute units.
  * out6[0] = workgroups per launch (256 threads each; a launch uses fewer where the
- * kernel's registers fit fewer workgroups per CU), out6[1] = low-bit chunks per
- * lane per row (per thread of the workgroup when out6[2] is 2), out6[2] = the kernel
- * kind (0: the generic stepping kernel, 1: a fixed-length kernel with one wave per
- * row, 2: a fixed-length kernel whose workgroup's four waves share each row, for
- * long rows that are few for the grid or at several tokens; its outputs add the four
- * waves' shares in a fixed order), out6[3] = where activation operands live across
- * rows (0: re-read from the q8 plane per row, 1: registers, 2: staged once per
- * workgroup in LDS), out6[4] = launches (one per group of up to 4 token columns),
- * out6[5] = rows in flight per wave. The kernel fields describe the first launch.
- * Host only. */
+ *   kernel's registers fit fewer workgroups per CU);
+ * out6[1] = low-bit chunks per lane per row (per thread of the workgroup when
+ *   out6[2] is 2);
+ * out6[2] = the kernel kind:
+ *   0 the generic stepping kernel;
+ *   1 a fixed-length kernel, one wave per row;
+ *   2 a fixed-length kernel whose workgroup's four waves share each row (long rows
+ *     that are few for the grid, or at several tokens); each output adds the four
+ *     waves' shares in a fixed order;
+ *   3 a fixed-length kernel with two rows per wave (2..4 tokens, K = 1024, 3072 or
+ *     5120, whose rows hold an odd multiple of 32 chunks, and at least 4 rows per wave
+ *     of its grid); each half of the wave takes one row's last chunk slot;
+ * out6[3] = where activation operands live across rows (0: re-read from the q8
+ *   plane per row, 1: registers, 2: staged once per workgroup in LDS);
+ * out6[4] = launches (one per group of up to 4 token columns);
+ * out6[5] = rows (kind 3: row pairs) in flight per wave.
+ * The kernel fields describe the first launch. Host only. */
 int q6k_mmvq_plan(int64_t N, int64_t K, int nt, int num_cu, int32_t *out6);
 
 /* The same for mmvq_kq_q8 with weight type `type` (Q6K_E_TYPE for an unknown one);

@@ -168,6 +168,17 @@ struct FmtKq {
         return o;
     }
 
+    // The same chunk `b` bytes further (a later row under one descriptor).
+    __device__ static Offs shifted(const Offs &o, uint32_t b)
+    {
+        Offs r;
+        r.qs = o.qs + b;
+        r.qh = o.qh + b;
+        r.sc = o.sc + b;
+        r.dm = o.dm + b;
+        return r;
+    }
+
     __device__ static W load(__amdgpu_buffer_rsrc_t r, const Offs &o)
     {
         W w;

@@ -85,16 +85,14 @@ __device__ __forceinline__ float dpp_add(float v)
     return v + dpp_mov<CTRL>(v);
 }
 
-// Sums over a wave64 of NT <= 4 per-lane values (one per token column). The
-// first steps transpose while they add: at the pair step a lane keeps the tokens
-// of its parity and hands the others to its partner, at the quad step likewise by
-// the second lane bit, so afterwards lane l carries only token (l & 3) (for NT = 2:
-// l & 1). Rotations by 4 and 8 lanes finish each 16-lane row; two lane-swaps add
-// the four rows. Lane l then holds the total of token (l & 3) (NT = 1: of the only
-// token). The adds always pair the same lanes in the same order, so results are
-// reproducible run to run.
+// Sums over each 16-lane row of NT <= 4 per-lane values (one per token column). The
+// first steps transpose while they add: at the pair step a lane keeps the tokens of
+// its parity and hands the others to its partner, at the quad step likewise by the
+// second lane bit, so afterwards lane l carries only token (l & 3) (for NT = 2:
+// l & 1). Rotations by 4 and 8 lanes finish each row: every lane then holds its
+// row's total of token (l & 3) (NT = 1: of the only token).
 template <int NT>
-__device__ __forceinline__ float reduce_tokens(const float (&a)[NT], uint32_t lane)
+__device__ __forceinline__ float row_sums(const float (&a)[NT], uint32_t lane)
 {
     static_assert(NT >= 1 && NT <= 4, "one to four token columns per reduction");
     float v;
@@ -115,18 +113,36 @@ __device__ __forceinline__ float reduce_tokens(const float (&a)[NT], uint32_t la
         }
     }
     v = dpp_add<0x124>(v);                           // row_ror:4
-    v = dpp_add<0x128>(v);                           // row_ror:8
-    // (each swap's two results are copied into plain integers before their bit
-    // casts: a bit cast applied straight to an element of the returned pair reads
-    // element 0 for both)
+    return dpp_add<0x128>(v);                        // row_ror:8
+}
+
+// The sum of v over the two 16-lane rows of each half wave (rows 0 + 1, rows 2 + 3).
+// v_permlane16_swap exchanges the odd rows of its first operand with the even rows
+// of its second, so with both operands v the two results hold (r0, r0, r2, r2) and
+// (r1, r1, r3, r3); their sum does not depend on which is which. (Each swap's two
+// results are copied into plain integers before their bit casts: a bit cast applied
+// straight to an element of the returned pair reads element 0 for both.)
+__device__ __forceinline__ float half_pair_sum(float v)
+{
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+
+// Sums over a wave64 of NT <= 4 per-lane values: the row sums, then two lane swaps
+// add the four rows. Lane l then holds the total of token (l & 3) (NT = 2: l & 1;
+// NT = 1: of the only token). The adds always pair the same lanes in the same order,
+// so results are reproducible run to run.
+template <int NT>
+__device__ __forceinline__ float reduce_tokens(const float (&a)[NT], uint32_t lane)
+{
+    float v = row_sums<NT>(a, lane);
     const unsigned u = __builtin_bit_cast(unsigned, v);
     const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);
     const unsigned h0 = h[0], h1 = h[1];
     v = __builtin_bit_cast(float, h0) + __builtin_bit_cast(float, h1);
-    const unsigned u2 = __builtin_bit_cast(unsigned, v);
-    const auto r = __builtin_amdgcn_permlane16_swap(u2, u2, false, false);
-    const unsigned r0 = r[0], r1 = r[1];
-    return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+    return half_pair_sum(v);
 }
 
 // The lane that holds token t's total after reduce_tokens.
@@ -518,6 +534,181 @@ __global__ __launch_bounds__(WG) void mmvq_split(const uint8_t *__restrict__ w,
         y[(size_t)t * ldy + row0 + j] = (p[0] + p[ws]) + (p[2u * ws] + p[3u * ws]);
     }
 }
+
+// Rows whose chunk count is an odd multiple of 32 (8 * nbe = 64 * (CPL - 1) + 32; K =
+// 5120: 160 chunks, 2.5 per lane) at several tokens. With one wave per row the upper
+// half of the wave idles in the last chunk slot: at three slots a sixth of the ALU
+// work, which at several tokens is what bounds the kernel. Here a wave takes the
+// rows A = 2p and B = 2p + 1 together and every lane does useful work in every slot:
+//  - buffer X, CPL slots: the full slots of row A in lanes 0-31 and of row B in lanes
+//    32-63, and the last, half slot (chunk 64 * (CPL - 1) + lane % 32) of that row;
+//  - buffer Y, CPL - 1 slots: the full slots of the other row.
+// One descriptor covers both rows; a lane's byte offsets pick its row (+stride for
+// B), so no per-lane selects. The activation operands are those of the one-row
+// kernel (the last slot's chunk is lane % 32 past 64 * (CPL - 1) in either half).
+// A = X over lanes 0-31 + Y over lanes 32-63 and B the other way round: each half
+// sums X and Y on its own (row sums, then rows 0 + 1, 2 + 3), then one lane swap
+// brings each half the other half's Y.
+template <int NT>
+__device__ __forceinline__ float reduce_pair(const float (&x)[NT], const float (&yv)[NT],
+                                             uint32_t lane)
+{
+    const float sx = half_pair_sum(row_sums<NT>(x, lane));
+    const float sy = half_pair_sum(row_sums<NT>(yv, lane));
+    // v_permlane32_swap exchanges the upper half of its first operand with the lower
+    // half of its second: with both sy, the first result holds the lower half's sum
+    // in both halves and the second the upper half's
+    const unsigned u = __builtin_bit_cast(unsigned, sy);
+    const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const unsigned lo = h[0], hi = h[1];
+    return sx + __builtin_bit_cast(float, lane < 32u ? hi : lo);
+}
+
+template <class F, int NT, int CPL>
+struct PairState {
+    typename F::Offs ox[CPL], oy[CPL > 1 ? CPL - 1 : 1];
+    uint32_t Q[CPL];
+    typename F::Act act[CPL][NT];
+};
+
+template <class F, int CPL>
+struct PairBufs {
+    typename F::W X[CPL], Y[CPL > 1 ? CPL - 1 : 1];
+};
+
+template <class F, int CPL>
+struct PairRing {
+    PairBufs<F, CPL> A, B, C;
+};
+
+template <class F, int NT, int CPL>
+__device__ __forceinline__ void pair_init(PairState<F, NT, CPL> &st, uint32_t lane,
+                                          uint32_t nbe, uint32_t stride, const int8_t *qs,
+                                          const uint16_t *d8, uint32_t K)
+{
+    const uint32_t bx = lane < 32u ? 0u : stride, by = lane < 32u ? stride : 0u;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const uint32_t Q = i < CPL - 1 ? lane + 64u * i : 64u * (CPL - 1) + (lane & 31u);
+        const typename F::Offs o = F::offsets(Q, nbe);
+        st.Q[i] = Q;
+        st.ox[i] = F::shifted(o, bx);
+        if (i < CPL - 1)
+            st.oy[i] = F::shifted(o, by);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            st.act[i][t] = F::act(qs + (size_t)t * K, d8 + (size_t)t * (K / 32), Q);
+    }
+}
+
+// Pair p's loads: rows 2p and 2p + 1 below N under one descriptor (pairs past the
+// end: an empty one, whose loads return zeros without a memory request).
+template <class F, int NT, int CPL>
+__device__ __forceinline__ void load_pair(PairBufs<F, CPL> &b, const uint8_t *w, uint32_t p,
+                                          uint32_t N, uint32_t stride,
+                                          const PairState<F, NT, CPL> &st)
+{
+    const uint32_t r0 = 2u * p;
+    const uint32_t rows = r0 < N ? (N - r0 < 2u ? N - r0 : 2u) : 0u;
+    const __amdgpu_buffer_rsrc_t r = buf_desc(w + (size_t)(rows ? r0 : 0u) * stride, rows * stride);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+        b.X[i] = F::load(r, st.ox[i]);
+#pragma unroll
+    for (int i = 0; i < CPL - 1; ++i)
+        b.Y[i] = F::load(r, st.oy[i]);
+}
+
+template <class F, int NT, int CPL>
+__device__ __forceinline__ void finish_pair(const PairBufs<F, CPL> &b,
+                                            const PairState<F, NT, CPL> &st, float *y,
+                                            uint32_t ldy, uint32_t p, uint32_t N, uint32_t lane)
+{
+    float ax[NT], ay[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        ax[t] = 0.0f;
+        ay[t] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            ax[t] = F::accumulate(ax[t], b.X[i], st.act[i][t], st.Q[i], true);
+            if (i < CPL - 1)
+                ay[t] = F::accumulate(ay[t], b.Y[i], st.act[i][t], st.Q[i], true);
+        }
+    }
+    const float s = reduce_pair<NT>(ax, ay, lane);
+    // lanes 0-31 hold row 2p, lanes 32-63 row 2p + 1 (token lane % 32 in each half)
+    const uint32_t row = 2u * p + (lane >> 5);
+    uint32_t t;
+    if (stores_token<NT>(lane & 31u, t) && row < N)
+        y[(size_t)t * ldy + row] = s;
+}
+
+#define PAIR_STEP(NB, NEXT, CB, P)                                                              \
+    do {                                                                                        \
+        load_pair(b.NB, w, NEXT, N, stride, st);                                                \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        finish_pair<F, NT, CPL>(b.CB, st, y, ldy, P, N, lane);                                  \
+    } while (0)
+
+template <class F, int NT, int CPL, int DEPTH>
+__global__ __launch_bounds__(WG) void mmvq_pairs(const uint8_t *__restrict__ w,
+                                                 const int8_t *__restrict__ qs,
+                                                 const uint16_t *__restrict__ d8,
+                                                 float *__restrict__ y, uint32_t N, uint32_t nbe,
+                                                 uint32_t stride, uint32_t K, uint32_t ldy)
+{
+    static_assert(DEPTH >= 1 && DEPTH <= 3, "one to three pairs in flight");
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = blockIdx.x * WAVES_PER_WG + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t nw = gridDim.x * WAVES_PER_WG;
+    const uint32_t P = (N + 1u) / 2u;
+    PairState<F, NT, CPL> st;
+    pair_init(st, lane, nbe, stride, qs, d8, K);
+    if (wave >= P)
+        return;
+    PairRing<F, CPL> b;
+    uint32_t p = wave;
+    if constexpr (DEPTH == 1) {
+        for (; p < P; p += nw) {
+            load_pair(b.A, w, p, N, stride, st);
+            __builtin_amdgcn_sched_barrier(0);
+            finish_pair<F, NT, CPL>(b.A, st, y, ldy, p, N, lane);
+        }
+    } else if constexpr (DEPTH == 2) {
+        load_pair(b.A, w, p, N, stride, st);
+        for (;;) {
+            const uint32_t p1 = p + nw, p2 = p1 + nw;
+            PAIR_STEP(B, p1, A, p);
+            if (p1 >= P)
+                break;
+            PAIR_STEP(A, p2, B, p1);
+            if (p2 >= P)
+                break;
+            p = p2;
+        }
+    } else {
+        load_pair(b.A, w, p, N, stride, st);
+        load_pair(b.B, w, p + nw, N, stride, st);
+        for (;;) {
+            const uint32_t p1 = p + nw, p2 = p1 + nw, p3 = p2 + nw;
+            PAIR_STEP(C, p2, A, p);
+            if (p1 >= P)
+                break;
+            PAIR_STEP(A, p3, B, p1);
+            if (p2 >= P)
+                break;
+            PAIR_STEP(B, p3 + nw, C, p2);
+            if (p3 >= P)
+                break;
+            p = p3;
+        }
+    }
+}
+#undef PAIR_STEP
 
 // RMSNorm -> q8 -> GEMV in one kernel, for the shapes whose activation operands
 // stay in registers. Every workgroup normalizes and quantizes the NT activation
@@ -1098,6 +1289,60 @@ hipError_t dispatch_split(int cpl, int num_cu, hipStream_t s, const GemvArgs &a)
     }
 }
 
+// Pairs of rows (mmvq_pairs) at 2..4 tokens when a row's chunk count is an odd
+// multiple of 32 with at most 3 chunks per lane (K = 1024, 3072, 5120) and the pairs
+// fill the grid at least twice over. Measured against one wave per row
+// (graph-replayed GEMV, one MI355X): lm_head 152064 x 5120 at 2 / 3 / 4 tokens
+// 97.3 -> 92.6, 104.5 -> 96.2, 110.6 -> 108.3 us; q4_K 27648 x 5120 at 4 tokens
+// 23.9 -> 21.8; q5_K 27648 x 5120 at 2 tokens 22.5 -> 20.5; q6_K 16384 x 3072 at 4
+// tokens 13.2 -> 11.2. At 4 and 5 chunks per lane (K = 7168, 9216) the pair's
+// registers cost more than the idle half slot and it measured 3-25 % slower; with
+// fewer pairs than waves (attn_v 1024 rows at 4 tokens: 4.3 -> 4.9 us) the halved
+// wave count loses. Depth 2 (two pairs in flight) at one workgroup per CU.
+constexpr int PAIRS_MAX_CPL = 3;
+
+constexpr RowsCfg pairs_cfg(int type, int nt, int cpl)
+{
+    (void)type;
+    (void)nt;
+    (void)cpl;
+    return RowsCfg{2, ACT_REGS, 1};
+}
+
+bool pairs_ok(int type, int nt, int cpl, int64_t N, int64_t K, int num_cu)
+{
+    const int n = nt < MAX_NT_KERNEL ? nt : MAX_NT_KERNEL;
+    if (n < 2 || cpl > PAIRS_MAX_CPL || (K / 256 * 8) % 64 != 32)
+        return false;
+    const int64_t waves = (int64_t)num_cu * pairs_cfg(type, n, cpl).wg_per_cu * WAVES_PER_WG;
+    return (N + 1) / 2 >= 2 * waves;
+}
+
+template <class F, int NT, int CPL>
+hipError_t launch_pairs(int num_cu, hipStream_t s, GemvArgs a)
+{
+    constexpr RowsCfg k = pairs_cfg(F::TYPE, NT, CPL);
+    const void *kern = (const void *)mmvq_pairs<F, NT, CPL, k.depth>;
+    const int fit = wg_fit(kern);
+    if (fit < 1)
+        return hipErrorInvalidValue;
+    const uint32_t grid = grid_for((a.N + 1u) / 2u, num_cu, k.wg_per_cu < fit ? k.wg_per_cu : fit);
+    void *args[] = {(void *)&a.w, (void *)&a.qs, (void *)&a.d8, (void *)&a.y, (void *)&a.N,
+                    (void *)&a.nbe, (void *)&a.stride, (void *)&a.K, (void *)&a.ldy};
+    return hipLaunchKernel(kern, dim3(grid), dim3(WG), args, 0, s);
+}
+
+template <class F, int NT>
+hipError_t dispatch_pairs(int cpl, int num_cu, hipStream_t s, const GemvArgs &a)
+{
+    switch (cpl) {
+    case 1: return launch_pairs<F, NT, 1>(num_cu, s, a);
+    case 2: return launch_pairs<F, NT, 2>(num_cu, s, a);
+    case 3: return launch_pairs<F, NT, 3>(num_cu, s, a);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 template <class F>
 hipError_t launch_mmvq_fmt(const uint8_t *w, const uint8_t *q8, float *y, int64_t N, int64_t K,
                            int nt, int num_cu, hipStream_t s)
@@ -1119,7 +1364,13 @@ hipError_t launch_mmvq_fmt(const uint8_t *w, const uint8_t *q8, float *y, int64_
         a.K = (uint32_t)K;
         a.ldy = (uint32_t)N;
         hipError_t e;
-        if (split_ok(F::TYPE, n, cpl, N, num_cu)) {
+        if (pairs_ok(F::TYPE, n, cpl, N, K, num_cu)) {
+            switch (n) {
+            case 2: e = dispatch_pairs<F, 2>(cpl, num_cu, s, a); break;
+            case 3: e = dispatch_pairs<F, 3>(cpl, num_cu, s, a); break;
+            default: e = dispatch_pairs<F, 4>(cpl, num_cu, s, a); break;
+            }
+        } else if (split_ok(F::TYPE, n, cpl, N, num_cu)) {
             switch (n) {
             case 1: e = dispatch_split<F, 1>(cpl, num_cu, s, a); break;
             case 2: e = dispatch_split<F, 2>(cpl, num_cu, s, a); break;
@@ -1234,6 +1485,14 @@ MmvqPlan plan_mmvq(int type, int64_t N, int64_t K, int nt, int num_cu)
     p.unrolled = p.cpl <= MAX_CPL;
     p.launches = (nt + MAX_NT_KERNEL - 1) / MAX_NT_KERNEL;
     const int nt0 = nt < MAX_NT_KERNEL ? nt : MAX_NT_KERNEL;
+    if (pairs_ok(type, nt0, p.cpl, N, K, num_cu)) {
+        p.paired = true;
+        const RowsCfg c = pairs_cfg(type, nt0, p.cpl);
+        p.act_mode = c.mode;
+        p.depth = c.depth;
+        p.grid = grid_for((N + 1) / 2, num_cu, c.wg_per_cu);
+        return p;
+    }
     if (split_ok(type, nt0, p.cpl, N, num_cu)) {
         p.shared = true;
         p.cpl = (p.cpl + 3) / 4;

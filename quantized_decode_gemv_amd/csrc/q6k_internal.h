@@ -16,6 +16,7 @@ struct MmvqPlan {
     bool unrolled = false;  // a fixed-CPL kernel (else the generic stepping kernel)
     bool shared = false;    // the rows shared by a workgroup's four waves (cpl is then
                             // per thread of the 256)
+    bool paired = false;    // two rows per wave, the last chunk slot split between them
     int act_mode = 0;       // activation operands across rows: 0 re-read per row,
                             // 1 registers, 2 staged in LDS once per workgroup
     int launches = 0;       // one launch per group of up to 4 token columns

@@ -193,6 +193,17 @@ struct FmtQ6K {
         return o;
     }
 
+    // The same chunk `b` bytes further (a later row under one descriptor).
+    __device__ static Offs shifted(const Offs &o, uint32_t b)
+    {
+        Offs r;
+        r.ql = o.ql + b;
+        r.qh = o.qh + b;
+        r.sc = o.sc + b;
+        r.d = o.d + b;
+        return r;
+    }
+
     // Low/high bits are streamed (non-temporal); the scale group and d keep the
     // default policy (each 64-byte line of them is touched by three load
     // instructions of the same row).

@@ -191,11 +191,32 @@ def test_plan_shared_rows_rule(qtype, nbe, N, nt):
     assert p["grid"] == -(-N // R) and p["act_mode"] == 1 and p["depth"] == (2 if wpc == 2 else 3)
 
 
+@pytest.mark.parametrize("qtype", [14, 12, 13])
+@pytest.mark.parametrize("nbe", list(range(1, 41)))
+@pytest.mark.parametrize("nt", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("N", [1000, 4094, 4095, 152064])
+def test_plan_pairs_rule(qtype, nbe, nt, N):
+    # two rows per wave at 2..4 tokens (per launch) when a row has an odd multiple of
+    # 32 chunks, at most 3 chunks per lane, and at least two pairs per wave of the
+    # grid (one workgroup per CU: 1024 waves on 256 CUs)
+    p = q.mmvq_plan(N, 256 * nbe, nt, 256, qtype)
+    expect = (min(nt, 4) >= 2 and (8 * nbe) % 64 == 32 and -(-8 * nbe // 64) <= 3
+              and (N + 1) // 2 >= 2048)
+    assert p["paired"] == expect
+    if expect:
+        pairs = (N + 1) // 2
+        assert p["cpl"] == -(-8 * nbe // 64) and p["grid"] == min(-(-pairs // 4), 256)
+        assert p["depth"] == 2 and p["act_mode"] == 1
+
+
 @pytest.mark.parametrize("N", [1, 2, 3, 63, 64, 65, 1023, 1024, 1025, 4096, 152064])
 @pytest.mark.parametrize("nt", [1, 2, 4])
 def test_plan_grid_is_whole_cus_or_one_wave_per_row(N, nt):
     p = q.mmvq_plan(N, 5120, nt, 256)
-    waves_needed = -(-N // 4)
+    # one wave per row, or per pair of rows (K = 5120 at several tokens, enough rows)
+    assert p["paired"] == (nt >= 2 and (N + 1) // 2 >= 2 * 1024)
+    units = -(-N // 2) if p["paired"] else N
+    waves_needed = -(-units // 4)
     assert p["grid"] == waves_needed or (p["grid"] % 256 == 0 and p["grid"] < waves_needed)
 
 

@@ -116,6 +116,22 @@ def test_shared_rows_random(qtype, N, nbe, nt):
     check_y(y, y_or, A, f"{NAMES[qtype]} shared N={N} nbe={nbe} nt={nt}")
 
 
+@pytest.mark.parametrize("qtype", TYPES, ids=_ids)
+@pytest.mark.parametrize("nbe", [4, 12, 20])
+@pytest.mark.parametrize("N,nt", [(4095, 2), (4097, 4), (6001, 3)])
+def test_pairs_random(qtype, nbe, N, nt):
+    # two rows per wave, the last chunk slot split between them
+    K = 256 * nbe
+    assert q.mmvq_plan(N, K, nt, 256, qtype)["paired"]
+    raw = q6ksynth.raw_kq(qtype, N, K, seed=N * 3 + nbe + nt + qtype)
+    dpl = kq_dpl_from_raw(qtype, raw, N, K)
+    x = np.stack([q6ksynth.activation("outlier", K, 1500 + c) for c in range(nt)])
+    qs, d = oracle.quant_q8(x)
+    y = run_kq(qtype, dpl, make_plane(qs, d), N, K, nt)
+    y_or, A = oracle.kq_mmvq(qtype, oracle.RAW, raw, N, K, qs, d)
+    check_y(y, y_or, A, f"{NAMES[qtype]} pairs N={N} nbe={nbe} nt={nt}")
+
+
 def _uniform_block(qtype, code, sc, m, d, dmin):
     blk = blank(qtype, 1)[0]
     set_d(qtype, blk, d, dmin)

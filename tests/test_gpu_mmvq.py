@@ -127,6 +127,23 @@ def test_shared_rows_random(N, nbe, nt):
     check_y(y, y_or, A, f"N={N} nbe={nbe} nt={nt}")
 
 
+# Two rows per wave (2..4 tokens, rows of an odd multiple of 32 chunks: nbe 4, 12, 20):
+# every chunk count per lane 1..3, an odd N (the last pair has one row), and nt = 5 (a
+# paired launch of 4 tokens, then a one-wave launch of 1).
+@pytest.mark.parametrize("nbe", [4, 12, 20])
+@pytest.mark.parametrize("N,nt", [(4095, 2), (4097, 3), (8192, 4), (4099, 5)])
+def test_pairs_random(nbe, N, nt):
+    K = 256 * nbe
+    assert q.mmvq_plan(N, K, nt, 256)["paired"]
+    raw = q6ksynth.raw_q6k(N, K, seed=N * 3 + nbe + nt)
+    dpl = dpl_from_raw(raw, N, K)
+    x = np.stack([q6ksynth.activation("outlier", K, 1400 + c) for c in range(nt)])
+    qs, d = oracle.quant_q8(x)
+    y = run_mmvq(dpl, make_plane(qs, d), N, K, nt)
+    y_or, A = oracle.mmvq(oracle.RAW, raw, N, K, qs, d)
+    check_y(y, y_or, A, f"pairs N={N} nbe={nbe} nt={nt}")
+
+
 @pytest.mark.parametrize("q0", [0, 1, 31, 33, 63])
 @pytest.mark.parametrize("nbe,block", [(1, 0), (4, 3)])
 def test_onehot_diagonal(q0, nbe, block):
