@@ -58,8 +58,12 @@ def _fill(producer, b, K, nt, seed):
         b["x"].copy_(torch.from_numpy(x))
 
 
+# the GEMV kinds: one wave per row, row pairs (8192 x 5120 at 4 tokens), rows shared
+# by a workgroup (3584 x 18944, 3000 x 13824 at 4 tokens), the generic stepping kernel
 @pytest.mark.parametrize("producer,N,K,nt", [("rmsnorm", 4096, 5120, 1), ("rmsnorm", 2048, 5120, 4),
-                                             ("swiglu", 1024, 13824, 1), ("quant", 64, 1024, 2),
+                                             ("rmsnorm", 8192, 5120, 4),
+                                             ("swiglu", 1024, 13824, 1), ("swiglu", 3584, 18944, 1),
+                                             ("quant", 64, 1024, 2), ("quant", 3000, 13824, 4),
                                              ("quant", 333, 256 * 97, 5),
                                              ("fused", 4096, 5120, 1), ("fused", 1024, 5120, 2),
                                              ("formb", 4096, 5120, 1)])
