@@ -1258,12 +1258,12 @@ hipError_t launch_split(int num_cu, hipStream_t s, GemvArgs a)
     constexpr RowsCfg k = split_cfg(F::TYPE, NT, CPL4);
     const void *kern = (const void *)mmvq_split<F, NT, CPL4, k.depth, k.mode>;
     const uint32_t acts = k.mode == ACT_LDS ? act_lds_bytes(NT, 8u * a.nbe) : 0u;
+    // split_ok bounds R by SPLIT_MAX_R at the table's workgroups per CU; a lower
+    // occupancy clamp only raises R (the shares' LDS, 16 * NT * R bytes, stays small)
     int wpc = k.wg_per_cu;
     uint32_t R = 0, lds = 0;
     for (;;) {
         R = split_rows(a.N, num_cu, wpc);
-        if (R > SPLIT_MAX_R)
-            return hipErrorInvalidValue;
         lds = acts + 16u * (uint32_t)NT * R;
         const int fit = wg_fit(kern, lds);
         if (fit < 1)
