@@ -483,7 +483,7 @@ __global__ __launch_bounds__(WG) void mmvq_rows(const uint8_t *__restrict__ w,
 // set the time, and each row's loads wait a whole memory latency. Here every wave has
 // R rows of a quarter the bytes, R is the same for every workgroup but the last, and
 // the chunks per lane fall to what the one-wave rows of lm_head have.
-// LDS: the ACT_LDS operands (if any), then the shares, 4 * NT * R floats.
+// LDS: the shares, 4 * NT * R floats.
 template <class F, int NT, int CPL, int DEPTH, int AM>
 __global__ __launch_bounds__(WG) void mmvq_split(const uint8_t *__restrict__ w,
                                                  const int8_t *__restrict__ qs,
@@ -492,6 +492,7 @@ __global__ __launch_bounds__(WG) void mmvq_split(const uint8_t *__restrict__ w,
                                                  uint32_t stride, uint32_t K, uint32_t ldy,
                                                  uint32_t R)
 {
+    static_assert(AM == ACT_REGS, "a thread's 2-3 chunks keep their operands in registers");
     extern __shared__ uint4 s_split[];
     const uint32_t row0 = blockIdx.x * R;
     if (row0 >= N)
@@ -499,29 +500,14 @@ __global__ __launch_bounds__(WG) void mmvq_split(const uint8_t *__restrict__ w,
     const uint32_t nr = N - row0 < R ? N - row0 : R;
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t C = 8u * nbe;
     const uint8_t *wb = w + (size_t)row0 * stride;
-    float *part = reinterpret_cast<float *>(
-        s_split + (AM == ACT_LDS ? 3u * (uint32_t)NT * (C + 1u) : 0u));
+    float *part = reinterpret_cast<float *>(s_split);
     float *share = part + wv * (uint32_t)NT * R;
     LaneState<F, NT, CPL, AM> st;
     RowBufs<F, CPL> bufs;
     lane_chunks<F, NT, CPL, AM, 256u>(st, threadIdx.x, nbe);
-    if constexpr (AM == ACT_LDS) {
-#pragma unroll
-        for (int i = 0; i < CPL; ++i)
-            st.ent[i] = st.live[i] ? st.Q[i] : C;
-        st.lds = s_split;
-        st.tstride = C + 1u;
-        st.plane = (uint32_t)NT * (C + 1u);
-        prime_rows<F, NT, CPL, 0, DEPTH - 1, AM>(bufs, wb, 0u, 1u, nr, stride, st);
-        __builtin_amdgcn_sched_barrier(0);
-        stage_acts<F, NT>(s_split, qs, d8, K, C);
-    } else {
-        if constexpr (AM == ACT_REGS)
-            lane_acts(st, qs, d8, K);
-        prime_rows<F, NT, CPL, 0, DEPTH - 1, AM>(bufs, wb, 0u, 1u, nr, stride, st);
-    }
+    lane_acts(st, qs, d8, K);
+    prime_rows<F, NT, CPL, 0, DEPTH - 1, AM>(bufs, wb, 0u, 1u, nr, stride, st);
     // the shares go where the one-wave kernel stores its outputs: token t of local
     // row j at share[t * R + j]
     stream_rows<F, NT, CPL, DEPTH, AM>(bufs, wb, 0u, 1u, nr, stride, st, qs, d8, K, share, R,
@@ -1257,14 +1243,13 @@ hipError_t launch_split(int num_cu, hipStream_t s, GemvArgs a)
 {
     constexpr RowsCfg k = split_cfg(F::TYPE, NT, CPL4);
     const void *kern = (const void *)mmvq_split<F, NT, CPL4, k.depth, k.mode>;
-    const uint32_t acts = k.mode == ACT_LDS ? act_lds_bytes(NT, 8u * a.nbe) : 0u;
     // split_ok bounds R by SPLIT_MAX_R at the table's workgroups per CU; a lower
     // occupancy clamp only raises R (the shares' LDS, 16 * NT * R bytes, stays small)
     int wpc = k.wg_per_cu;
     uint32_t R = 0, lds = 0;
     for (;;) {
         R = split_rows(a.N, num_cu, wpc);
-        lds = acts + 16u * (uint32_t)NT * R;
+        lds = 16u * (uint32_t)NT * R;
         const int fit = wg_fit(kern, lds);
         if (fit < 1)
             return hipErrorInvalidValue;
