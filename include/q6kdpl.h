@@ -142,7 +142,9 @@ int swiglu_quant_q8(const float *g, const float *u, float *y, void *q8, int64_t 
  * 16 codes (q - 32) and the 16 int8 activations of sub-block j ([D4-2] §3.2
  * Excerpt C, the per-unit accumulation; [D4-4] §3.2 Excerpt B, the dpl unit load).
  * Sub-block dots are exact; scaling and summation are f32 (error well inside
- * 1e-5 * sum|terms|). Every unit of every row is covered for every N, K, nt in
+ * 1e-5 * sum|terms|). The order of the f32 sums follows the kernel kind that
+ * q6k_mmvq_plan reports for the shape and is fixed for it, so a shape's results
+ * repeat bit for bit. Every unit of every row is covered for every N, K, nt in
  * range (no shape reaches a kernel that skips work; [D4-2] §2).
  * w_dpl: q6k_dpl_bytes(N, K) device bytes, 16-B aligned; q8: q8_plane_bytes(K, nt)
  * device bytes, 16-B aligned; y: float32 [nt][N] device, 16-B aligned, written. */
