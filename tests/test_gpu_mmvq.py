@@ -177,11 +177,13 @@ def test_zero_scale_rows_are_exactly_zero():
     check_y(y, y_or, A, "zero-scale rows")
 
 
-def test_side_stream_and_repeat_calls_agree():
-    N, K, nt = 2048, 5120, 1
+# one wave per row; row pairs; rows shared by a workgroup (one token and four)
+@pytest.mark.parametrize("N,K,nt", [(2048, 5120, 1), (8192, 5120, 4), (3584, 18944, 1),
+                                    (3000, 13824, 4)])
+def test_side_stream_and_repeat_calls_agree(N, K, nt):
     raw = q6ksynth.raw_q6k(N, K, seed=2)
     dpl = dpl_from_raw(raw, N, K)
-    x = q6ksynth.activation("outlier", K, 6)[None]
+    x = np.stack([q6ksynth.activation("outlier", K, 6 + c) for c in range(nt)])
     qs, d = oracle.quant_q8(x)
     plane = make_plane(qs, d)
     y1 = run_mmvq(dpl, plane, N, K, nt)
