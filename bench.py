@@ -88,6 +88,70 @@ def copy_calib(steps: int) -> None:
                       "launches": steps}), flush=True)
 
 
+def read_ceiling(sizes_mb, steps: int) -> None:
+    """The read ceiling by size: the probe library streams each size with the GEMV's
+    load form and row walk (4 KB rows, no arithmetic), `steps` launches per HIP graph
+    replay; the best of depths 1-4 and grids of 1-8 workgroups per CU is one JSON line
+    per size. Buffers rotate over
+    copies of at least 1 GiB in all, as the GEMV's weights do, so no launch reads
+    what the last one left in the caches."""
+    import ctypes
+    import torch
+    from quantized_decode_gemv_amd import build as libbuild
+    if not os.path.exists(libbuild.PROBE_LIB):
+        libbuild.build()
+    lib = ctypes.CDLL(libbuild.PROBE_LIB)
+    lib.q6k_read_probe.restype = ctypes.c_int
+    lib.q6k_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    dev = "cuda:0"
+    num_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    for mb in sizes_mb:
+        nbytes = int(mb * 1e6) // 4096 * 4096
+        copies = max(2, math.ceil(ROTATE_BYTES / nbytes))
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
+        best = None
+        for depth in (1, 2, 3, 4):
+            for wpc in (1, 2, 4, 8):
+                grid = num_cu * wpc
+
+                def launch(i, st):
+                    rc = lib.q6k_read_probe(bufs[i % copies].data_ptr(), nbytes, depth, grid,
+                                            sink.data_ptr(), st.cuda_stream)
+                    assert rc == 0, rc
+                # the launches are replayed from a HIP graph: a few-microsecond kernel
+                # launched from Python would measure the host's launch rate instead
+                side = torch.cuda.Stream()
+                with torch.cuda.stream(side):
+                    for i in range(copies):
+                        launch(i, side)
+                torch.cuda.synchronize()
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph, stream=side):
+                    for i in range(steps):
+                        launch(i, side)
+                graph.replay()
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                with torch.cuda.stream(side):
+                    e0.record(side)
+                    graph.replay()
+                    e1.record(side)
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / steps
+                del graph
+                if best is None or us < best[0]:
+                    best = (us, depth, grid)
+        us, depth, grid = best
+        print(json.dumps({"read_ceiling_bytes": nbytes, "us": round(us, 2),
+                          "TB_per_s": round(nbytes / us / 1e6, 3), "depth": depth,
+                          "grid": grid, "launches_per_graph": steps}), flush=True)
+        del bufs
+        torch.cuda.empty_cache()
+
+
 def cpu_baseline(w, raw, x, g, gate, up, nt: int, budget_s: float = 20.0) -> dict:
     """The oracle chain (the workload's producer, q8, GEMV) on the host over a row
     sample of the same matrix, single thread; the sample is sized to stay near
@@ -137,6 +201,8 @@ def main() -> int:
     ap.add_argument("--workload", default="lm_head")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
+    ap.add_argument("--read-ceiling", default=None, metavar="MB,MB,...",
+                    help="time the read probe at these sizes (MB) instead of the GEMV step")
     ap.add_argument("--path", choices=["fused", "split", "formb"], default="fused",
                     help="fused: one RMSNorm -> q8 -> GEMV call per step (RMSNorm workloads "
                          "only); split: the producer kernel, then the GEMV kernel; formb: "
@@ -160,6 +226,9 @@ def main() -> int:
 
     if args.copy_calib:
         copy_calib(args.steps)
+        return 0
+    if args.read_ceiling:
+        read_ceiling([float(v) for v in args.read_ceiling.split(",")], args.steps)
         return 0
 
     dev = "cuda:0"

@@ -13,6 +13,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libq6kdpl.so")
 SOURCES = ["abi.hip", "mmvq.hip", "producer.hip", "repack.hip"]
+# the read-bandwidth probe of the measurement harness (bench.py --read-ceiling), a
+# library of its own so the GEMV library holds only the path
+PROBE_LIB = os.path.join(PKG, "libq6kprobe.so")
+PROBE_SOURCES = ["read_probe.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -30,10 +34,10 @@ def sources():
     return [os.path.join(CSRC, s) for s in SOURCES]
 
 
-def build(verbose: bool = False) -> str:
+def _hipcc(srcs, out: str, verbose: bool) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *sources(), "-o", tmp]
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -43,8 +47,14 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + err)
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Builds the GEMV library and the measurement probe; returns the library path."""
+    _hipcc([os.path.join(CSRC, s) for s in PROBE_SOURCES], PROBE_LIB, verbose)
+    return _hipcc(sources(), LIB, verbose)
 
 
 if __name__ == "__main__":

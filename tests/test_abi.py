@@ -357,3 +357,23 @@ def test_form_b_rejects_bad_arguments():
     assert q.gate_up_swiglu_fused(13824, 5120) and not q.gate_up_swiglu_fused(64, 256 * 49)
     with pytest.raises(q.Q6kError):
         q.gate_up_swiglu_fused(48, 256)
+
+
+def test_read_probe_library_loads_and_rejects_bad_arguments():
+    # the measurement probe (bench.py --read-ceiling) is a library of its own; its
+    # argument checks run on the host before any GPU call
+    import ctypes
+    from quantized_decode_gemv_amd import build as libbuild
+    lib = ctypes.CDLL(libbuild.PROBE_LIB)
+    f = lib.q6k_read_probe
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_void_p]
+    good = 0x10000000
+    assert f(None, 1 << 20, 2, 256, good, None) == -1          # no buffer
+    assert f(good, 1 << 20, 2, 256, None, None) == -1          # no sink
+    assert f(good, 4095, 2, 256, good, None) == -1             # less than one row
+    assert f(good, 1 << 20, 0, 256, good, None) == -1          # depth 1..4
+    assert f(good, 1 << 20, 5, 256, good, None) == -1
+    assert f(good, 1 << 20, 2, 0, good, None) == -1            # no workgroups
+    assert f(good + 8, 1 << 20, 2, 256, good, None) == -1      # 16-B alignment
