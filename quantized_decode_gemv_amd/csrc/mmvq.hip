@@ -1103,7 +1103,7 @@ hipError_t launch(Kern kern, int num_cu, int wg_per_cu, hipStream_t s, GemvArgs 
 template <class F, int NT, int CPL>
 hipError_t launch_cpl(const RowsCfg &c, int num_cu, hipStream_t s, const GemvArgs &a)
 {
-    // the one (depth, hoist) pair rows_cfg picks for this type, NT and CPL is built,
+    // the one (depth, operand mode) pair rows_cfg picks for this type, NT and CPL is built,
     // for the token counts a launch of this CPL can have
     constexpr RowsCfg k = rows_cfg(F::TYPE, NT, CPL);
     if (c.depth != k.depth || c.mode != k.mode)

@@ -88,7 +88,9 @@ def test_subdots_bit_exact(N, K, nt):
 
 
 # chunks per lane change at nbe = 8k -> 8k+1; the unrolled/generic switch is at
-# nbe 96 -> 97; activation hoisting switches with nt * chunks-per-lane <= 6.
+# nbe 96 -> 97; the operand mode (registers or LDS), the shared rows (from 7 chunks
+# per lane) and the row pairs (nbe 4, 12, 20 at several tokens, enough rows) switch
+# with chunks per lane and tokens.
 EDGE_NBE = sorted({1, 2, 3, 7} | {8 * k for k in range(1, 13)} | {8 * k + 1 for k in range(0, 13)}
                   | {100, 128, 200})
 
