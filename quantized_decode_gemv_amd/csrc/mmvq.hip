@@ -1204,8 +1204,8 @@ hipError_t dispatch_fused(int cpl, int depth, std::integer_sequence<int, CPLS...
 //    wave (3584 x 18944 12.5 -> 11.1-11.5 us); with 5 or more it loses 2-4 %
 //    (5120 x 13824, 8192 x 13824, 16384 x 18944).
 // Its chunks per lane are then ceil(cpl / 4) = 2 or 3, its rows per workgroup at most
-// SPLIT_MAX_R (N <= 131072 at two workgroups per CU); longer rows (cpl > MAX_CPL)
-// take the generic stepping kernel.
+// SPLIT_MAX_R (N <= 131072 at two workgroups per CU, 65536 at one); longer rows
+// (cpl > MAX_CPL) take the generic stepping kernel.
 constexpr int64_t SPLIT_ROWS_PER_WAVE = 4;
 constexpr uint32_t SPLIT_MAX_R = 256;   // rows per workgroup (LDS: 16 * nt * R bytes)
 
