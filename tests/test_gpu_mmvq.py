@@ -146,6 +146,41 @@ def test_pairs_random(nbe, N, nt):
     check_y(y, y_or, A, f"pairs N={N} nbe={nbe} nt={nt}")
 
 
+# Matrices past 4 GiB of dpl rows: the rows past byte 2^32 need wider than 32-bit
+# offsets, in the repack and in the GEMV kinds that reach such sizes -- lm_head-width
+# rows (2^20 of them) at one token (one wave per row) and four (row pairs); tall-K
+# rows at four tokens (operands staged in LDS); rows of 100 super-blocks (the generic
+# stepping kernel). The raw blocks are made on the device from a seeded generator
+# (uniform bytes, d = fp16(|N(0,1)| * 1e-3)); the oracle checks the first and last
+# rows and a seeded sample between them.
+@pytest.mark.parametrize("N,K,nt", [(1 << 20, 5120, 1), (1 << 20, 5120, 4),
+                                    (280000, 18944, 4), (210000, 25600, 1)])
+def test_matrix_past_4gib(N, K, nt):
+    nbe = K // 256
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(4242)
+    raw = torch.randint(0, 256, (N, nbe, 210), dtype=torch.uint8, device=DEV, generator=gen)
+    d = (torch.randn((N, nbe), device=DEV, generator=gen).abs() * 1e-3).half()
+    raw[:, :, 208:210] = d.view(torch.uint8).view(N, nbe, 2)
+    dpl = torch.empty(q.q6k_dpl_bytes(N, K), dtype=torch.uint8, device=DEV)
+    q.repack_q6k_dpl(raw.view(-1), dpl, N, K)
+    assert dpl.numel() > (1 << 32)
+    x = np.stack([q6ksynth.activation("outlier", K, 1600 + c) for c in range(nt)])
+    qs, dd = oracle.quant_q8(x)
+    y = run_mmvq(dpl, make_plane(qs, dd), N, K, nt)
+    del dpl
+    rng = np.random.default_rng(4243)
+    rows = np.unique(np.concatenate([np.arange(256), np.arange(N - 512, N),
+                                     rng.integers(0, N, 512)]))
+    raw_h = raw[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    del raw
+    torch.cuda.empty_cache()
+    y_or, A = oracle.mmvq(oracle.RAW, raw_h.reshape(-1), rows.size, K, qs, dd,
+                          nthreads=oracle_threads())
+    worst = check_y(y[:, rows], y_or, A, f"past 4 GiB N={N} K={K} nt={nt}")
+    say(f"past 4 GiB N={N} K={K} nt={nt}: {rows.size} rows checked, max err/A = {worst:.3e}")
+
+
 @pytest.mark.parametrize("q0", [0, 1, 31, 33, 63])
 @pytest.mark.parametrize("nbe,block", [(1, 0), (4, 3)])
 def test_onehot_diagonal(q0, nbe, block):
