@@ -132,6 +132,39 @@ def test_pairs_random(qtype, nbe, N, nt):
     check_y(y, y_or, A, f"{NAMES[qtype]} pairs N={N} nbe={nbe} nt={nt}")
 
 
+# q4_K / q5_K matrices past 4 GiB of split-plane rows (K = 5120; 1.5M q4_K rows, 1.3M
+# q5_K rows): rows past byte 2^32 need wider offsets in the repack and the GEMV. Raw
+# blocks are made on the device from a seeded generator (uniform bytes, d and dmin =
+# fp16(|N(0,1)| * 1e-3)); the oracle checks the first and last rows and a sample.
+@pytest.mark.parametrize("qtype,N,nt", [(q.KQ_Q4_K, 1500000, 1), (q.KQ_Q5_K, 1300000, 2)],
+                         ids=["q4_K-1", "q5_K-2"])
+def test_matrix_past_4gib(qtype, N, nt):
+    K = 5120
+    nbe, B = K // 256, q.kq_block_bytes(qtype)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(4343 + qtype)
+    raw = torch.randint(0, 256, (N, nbe, B), dtype=torch.uint8, device=DEV, generator=gen)
+    dm = (torch.randn((N, nbe, 2), device=DEV, generator=gen).abs() * 1e-3).half()
+    raw[:, :, 0:4] = dm.view(torch.uint8).view(N, nbe, 4)
+    dpl = torch.empty(q.kq_dpl_bytes(qtype, N, K), dtype=torch.uint8, device=DEV)
+    q.repack_kq_dpl(qtype, raw.view(-1), dpl, N, K)
+    assert dpl.numel() > (1 << 32)
+    x = np.stack([q6ksynth.activation("outlier", K, 1700 + c) for c in range(nt)])
+    qs, d = oracle.quant_q8(x)
+    y = run_kq(qtype, dpl, make_plane(qs, d), N, K, nt)
+    del dpl
+    rng = np.random.default_rng(4344 + qtype)
+    rows = np.unique(np.concatenate([np.arange(256), np.arange(N - 512, N),
+                                     rng.integers(0, N, 512)]))
+    raw_h = raw[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    del raw
+    torch.cuda.empty_cache()
+    y_or, A = oracle.kq_mmvq(qtype, oracle.RAW, raw_h.reshape(-1), rows.size, K, qs, d,
+                             nthreads=oracle_threads())
+    worst = check_y(y[:, rows], y_or, A, f"{NAMES[qtype]} past 4 GiB N={N} nt={nt}")
+    say(f"{NAMES[qtype]} past 4 GiB N={N} nt={nt}: {rows.size} rows, max err/A = {worst:.3e}")
+
+
 def _uniform_block(qtype, code, sc, m, d, dmin):
     blk = blank(qtype, 1)[0]
     set_d(qtype, blk, d, dmin)
