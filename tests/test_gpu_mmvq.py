@@ -181,6 +181,20 @@ def test_matrix_past_4gib(N, K, nt):
     say(f"past 4 GiB N={N} K={K} nt={nt}: {rows.size} rows checked, max err/A = {worst:.3e}")
 
 
+# The longest row the boundary accepts (K = 2^20, 4096 super-blocks: the generic
+# stepping kernel), a few rows, one and several tokens.
+@pytest.mark.parametrize("nt", [1, 3])
+def test_longest_rows(nt):
+    N, K = 7, 1 << 20
+    raw = q6ksynth.raw_q6k(N, K, seed=77 + nt)
+    dpl = dpl_from_raw(raw, N, K)
+    x = np.stack([q6ksynth.activation("outlier", K, 1800 + c) for c in range(nt)])
+    qs, d = oracle.quant_q8(x)
+    y = run_mmvq(dpl, make_plane(qs, d), N, K, nt)
+    y_or, A = oracle.mmvq(oracle.RAW, raw, N, K, qs, d)
+    check_y(y, y_or, A, f"K=2^20 nt={nt}")
+
+
 @pytest.mark.parametrize("q0", [0, 1, 31, 33, 63])
 @pytest.mark.parametrize("nbe,block", [(1, 0), (4, 3)])
 def test_onehot_diagonal(q0, nbe, block):

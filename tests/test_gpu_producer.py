@@ -50,7 +50,7 @@ def test_quant_q8_closed_form(case):
     assert np.array_equal(qs[0], qexp) and int(d[0, 0]) == d16
 
 
-@pytest.mark.parametrize("K", [32, 256, 1024, 5120, 13824, 18944])
+@pytest.mark.parametrize("K", [32, 256, 1024, 5120, 13824, 18944, 1 << 20])
 @pytest.mark.parametrize("nt", [1, 4, 5])
 @pytest.mark.parametrize("kind", ["normal", "outlier", "swiglu"])
 def test_quant_q8_bit_exact(K, nt, kind):
@@ -80,8 +80,9 @@ def test_quant_q8_wide_dynamic_range():
 
 # every register-resident variant's edge (K/4 = 512, 1024, 2048, 4096, 8192 float4s)
 # and the looping form past K = 32768
+# up to the longest row the boundary accepts (K = 2^20)
 RMS_K = [256, 1024, 2048, 2080, 4096, 4128, 5120, 8192, 8224, 13824, 16384, 16416, 18944,
-         32768, 32800, 40960]
+         32768, 32800, 40960, 1 << 20]
 
 
 @pytest.mark.parametrize("K", RMS_K)
@@ -123,7 +124,7 @@ def _swiglu_tol(y_or):
     return 4 * np.spacing(np.abs(y_or).astype(np.float32)).astype(np.float64)
 
 
-@pytest.mark.parametrize("K", [32, 256, 5120, 13824, 18944])
+@pytest.mark.parametrize("K", [32, 256, 5120, 13824, 18944, 1 << 20])
 @pytest.mark.parametrize("nt", [1, 4, 5])
 def test_swiglu_quant_q8(K, nt):
     g, u = (np.stack(a) for a in zip(*[q6ksynth.swiglu_pair(K, 800 + c) for c in range(nt)]))
