@@ -80,15 +80,29 @@ def check_y(y: np.ndarray, y_or: np.ndarray, A: np.ndarray, what: str) -> float:
     return worst
 
 
-def check_plane_vs_oracle_chain(y_gpu, y_or, qs, d16, qs_or, d_or, what: str) -> dict:
-    """Compare a producer's q8 plane with the oracle chain's, block by block.
+def check_plane_exact(y_gpu, qs, d16, what: str) -> None:
+    """A producer's q8 plane must be the oracle quantizer applied to the producer's
+    own y, bit for bit, on every block (the quantizer is a per-block function of its
+    32 inputs)."""
+    qs_o, d_o = oracle.quant_q8(np.ascontiguousarray(y_gpu, dtype=np.float32))
+    bad = np.flatnonzero(np.any(qs.reshape(-1, 32) != qs_o.reshape(-1, 32), axis=1)
+                         | (d16.reshape(-1) != d_o.reshape(-1)))
+    assert bad.size == 0, (f"{what}: q8 plane differs from the oracle quantizer of the "
+                           f"producer's own y in {bad.size} blocks (first {bad[:4]})")
 
-    Blocks whose 32 producer outputs equal the oracle's bit for bit must give the
-    same q8 bytes (the quantizer is a per-block function of its inputs). The RMSNorm
-    reduction order is left open by the pages, so a block holding an output that
-    differs in its last bits may differ by at most one code per element and one
-    fp16 step in its scale. Returns counts for the report.
+
+def check_plane_vs_oracle_chain(y_gpu, y_or, qs, d16, qs_or, d_or, what: str) -> dict:
+    """Check a producer's q8 plane against the oracle.
+
+    First, bit for bit against the oracle quantizer applied to the producer's own y
+    (check_plane_exact). Then against the oracle chain (the oracle quantizer applied
+    to the oracle's y), block by block: blocks whose 32 producer outputs equal the
+    oracle's bit for bit must give the same q8 bytes; the RMSNorm reduction order
+    is left open by the pages, so a block holding an output that differs in its last
+    bits may differ by at most one code per element and one fp16 step in its scale.
+    Returns counts for the report.
     """
+    check_plane_exact(y_gpu, qs, d16, what)
     nt, K = qs.shape
     yb = y_gpu.reshape(nt, K // 32, 32)
     ob = y_or.reshape(nt, K // 32, 32)
@@ -101,3 +115,31 @@ def check_plane_vs_oracle_chain(y_gpu, y_or, qs, d16, qs_or, d_or, what: str) ->
     assert dq[~same_in].max(initial=0) <= 1 and dd[~same_in].max(initial=0) <= 1, what
     return dict(blocks=int(same_in.size), blocks_inputs_differ=int((~same_in).sum()),
                 codes_differ=int((qs != qs_or).sum()))
+
+
+def oracle_gemv(qtype: int, raw, N: int, K: int, qs, d16):
+    """The oracle GEMV (raw rows) of any weight type: (y, A)."""
+    if qtype == q.KQ_Q6_K:
+        return oracle.mmvq(oracle.RAW, raw, N, K, qs, d16, nthreads=oracle_threads())
+    return oracle.kq_mmvq(qtype, oracle.RAW, raw, N, K, qs, d16, nthreads=oracle_threads())
+
+
+def check_y_on_plane(y, raw, qs, d16, N: int, K: int, what: str, qtype: int = None) -> float:
+    """y of the GPU's whole chain against the oracle GEMV run on the GPU's own q8
+    plane (qs, d16), so the check never depends on the producer matching the oracle
+    chain bit for bit. Returns the worst err / A."""
+    y_or, A = oracle_gemv(q.KQ_Q6_K if qtype is None else qtype, raw, N, K, qs, d16)
+    return check_y(np.asarray(y).reshape(y_or.shape), y_or, A, what)
+
+
+def swiglu_tol(y_or, g, u):
+    """The SwiGLU producer's f32 body g / (1 + expf(-g)) * u (D3-5 §3.2) against the
+    oracle's exactly rounded value: expf, 1 + e, the division and the product each
+    round once, so 4 ulp; and where expf(-g) overflows f32 (g below about -88.7) the
+    body gives g / inf = -0, while the exact value is below |g * u| * e^g < |g * u| *
+    2^-128, so an absolute term |g * u| * 2^-126 covers that tail (and any rounding in
+    the subnormal range)."""
+    y_or = np.asarray(y_or, np.float64)
+    gu = np.abs(np.asarray(g, np.float64) * np.asarray(u, np.float64)).reshape(y_or.shape)
+    return (4 * np.spacing(np.abs(y_or).astype(np.float32)).astype(np.float64)
+            + gu * 2.0 ** -126)

@@ -1,8 +1,10 @@
 """GPU parity of Form B (gate+up GEMV, SwiGLU and q8 of one token in one call).
 
-Its outputs must equal mmvq_kq_q8 followed by swiglu_quant_q8 bit for bit (both
-checked against the oracle by the other tests); gu is also checked against the
-oracle GEMV directly, and writes outside the outputs are caught by sentinels."""
+Its outputs must equal mmvq_kq_q8 followed by swiglu_quant_q8 bit for bit, and each
+is checked against the oracle directly: gu against the oracle GEMV, y against the
+oracle SwiGLU of the returned gate and up halves (4 ulp, the f32 body's roundings),
+and the q8 plane bit for bit against the oracle quantizer of the returned y. Writes
+outside the outputs are caught by sentinels."""
 import numpy as np
 import pytest
 import torch
@@ -10,7 +12,8 @@ import torch
 import oracle
 import q6ksynth
 import quantized_decode_gemv_amd as q
-from gpu_util import DEV, check_y, dev_u8, make_plane, oracle_threads, say
+from gpu_util import (DEV, check_plane_exact, check_y, dev_u8, make_plane, oracle_threads, say,
+                      swiglu_tol)
 
 pytestmark = pytest.mark.gpu
 
@@ -73,6 +76,7 @@ def test_form_b_equals_gemv_then_swiglu(qtype, Nh, K):
     x = q6ksynth.activation("outlier", K, 31 + Nh)[None]
     qs, d = oracle.quant_q8(x)
     plane = make_plane(qs, d)
+    ys = {}
     for with_y in (True, False):
         g1, y1, p1 = _form_b(qtype, dpl, plane, Nh, K, with_y)
         g2, y2, p2 = _split(qtype, dpl, plane, Nh, K)
@@ -80,9 +84,19 @@ def test_form_b_equals_gemv_then_swiglu(qtype, Nh, K):
         assert np.array_equal(p1, p2)
         if with_y:
             assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+            ys["y"] = y1
+    y1 = ys["y"]
     # gu against the oracle GEMV (from the oracle's own inputs)
     y_or, A = _oracle_gemv(qtype, raw, 2 * Nh, K, qs, d)
     check_y(g1[None], y_or, A, f"form B gu {NAMES[qtype]}")
+    # y against the oracle SwiGLU of the kernel's own gate and up totals
+    sw_or = oracle.swiglu(g1[None, :Nh], g1[None, Nh:])[0]
+    tol = swiglu_tol(sw_or, g1[:Nh], g1[Nh:])
+    assert np.all(np.abs(y1.astype(np.float64) - sw_or) <= tol), "form B y"
+    # the q8 plane against the oracle quantizer of the kernel's own y, bit for bit
+    check_plane_exact(y1[None], p1[:Nh].view(np.int8)[None], p1[Nh:].view(np.uint16)[None],
+                      f"form B q8 {NAMES[qtype]}")
+    say(f"  gu, y and q8 against the oracle; y bit-equal fraction {np.mean(y1 == sw_or):.4f}")
 
 
 def test_form_b_zero_gate_rows_give_zero_block():

@@ -4,15 +4,22 @@ in a HIP graph and replayed.
 The library queues plain kernel launches on the caller's stream (no allocation,
 no memset, no synchronisation), so torch's graph capture records them. Every
 replay is checked bitwise against eager execution of the same kernels, with new
-inputs copied in eagerly and the stream synchronised between replays.
+inputs copied in eagerly and the stream synchronised between replays, and against
+the oracle: the q8 plane bit for bit against the oracle quantizer of the replay's
+own producer output (its input row for the plain quantizer), the GEMV outputs
+against the oracle GEMV on the replay's own plane, and for Form B the SwiGLU output
+against the oracle SwiGLU of the replay's gate and up totals (4 ulp) and its q8
+plane against the oracle quantizer of that output.
 """
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import q6ksynth
 import quantized_decode_gemv_amd as q
-from gpu_util import DEV, dev_f32, dpl_from_raw, say
+from gpu_util import (DEV, check_plane_exact, check_y_on_plane, dev_f32, dpl_from_raw, say,
+                      split_plane, swiglu_tol)
 
 pytestmark = pytest.mark.gpu
 
@@ -92,9 +99,34 @@ def test_graph_replays_match_eager(producer, N, K, nt):
         got = y.clone()
         plane_g = b["plane"].clone()
         out_g = b["plane_out"].clone()
+        yn_g = b["yn"].clone()
         _step(producer, b, W, y, N, K, nt)          # eager, same inputs
         torch.cuda.synchronize()
         assert torch.equal(b["plane"], plane_g), f"replay {rep}: q8 plane differs from eager"
         assert torch.equal(b["plane_out"], out_g), f"replay {rep}: output plane differs"
         assert torch.equal(y, got), f"replay {rep}: y differs from eager"
-    say(f"graph {producer} N={N} K={K} nt={nt}: 5 replays bitwise equal to eager")
+        _check_replay_vs_oracle(producer, b, raw, got, plane_g, out_g, yn_g, N, K, nt,
+                                f"graph {producer} replay {rep}")
+    say(f"graph {producer} N={N} K={K} nt={nt}: 5 replays bitwise equal to eager and "
+        f"within the oracle's bounds")
+
+
+def _check_replay_vs_oracle(producer, b, raw, y, plane, plane_out, yn, N, K, nt, what):
+    qs, d = split_plane(plane, K, nt)
+    if producer in ("quant", "formb"):
+        src = b["x"].cpu().numpy()              # the plain quantizer's input row
+    else:
+        src = yn.cpu().numpy()                  # the producer's own output row
+    check_plane_exact(src, qs, d, what + " q8")
+    yh = y.cpu().numpy()
+    check_y_on_plane(yh, raw, qs, d, N, K, what + " y")
+    if producer == "formb":
+        Nh = N // 2
+        gu = yh.reshape(-1)
+        sw = yn.cpu().numpy().reshape(-1)[:Nh]
+        sw_or = oracle.swiglu(gu[None, :Nh], gu[None, Nh:])[0]
+        tol = swiglu_tol(sw_or, gu[:Nh], gu[Nh:])
+        assert np.all(np.abs(sw.astype(np.float64) - sw_or) <= tol), what + " swiglu"
+        po = plane_out.cpu().numpy()
+        check_plane_exact(sw[None], po[:Nh].view(np.int8)[None],
+                          po[Nh:Nh + Nh // 16].view(np.uint16)[None], what + " q8 out")
