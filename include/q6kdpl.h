@@ -20,9 +20,16 @@
  *    the null stream of the current device). They only queue work on `stream`
  *    and return without synchronising; results are visible after the stream is
  *    synchronised. Host entry points take host pointers and run synchronously.
- *  - The caller owns every buffer. The library allocates no memory, keeps no
- *    cache and reads no environment; calls are reentrant. Calls that share an
- *    output buffer must be ordered by the caller.
+ *  - The caller owns every buffer. The library allocates no memory, keeps no data
+ *    of any call and reads no environment; calls are reentrant. Calls that share
+ *    an output buffer must be ordered by the caller.
+ *  - Process-wide state: two tables, filled on first use and kept until the
+ *    process ends, both about the hardware and the kernels, never about a call's
+ *    data: the compute-unit count of each device (lock-free), and, per device,
+ *    kernel and dynamic LDS size, how many 256-thread workgroups of that kernel fit
+ *    on one compute unit (from hipOccupancyMaxActiveBlocksPerMultiprocessor, behind
+ *    a mutex; a kernel that needs more than 64 KB of LDS is first allowed it with
+ *    hipFuncSetAttribute). The grid of a launch is sized from them.
  *  - Sizes: K is the row length (number of weights per row), N the number of
  *    rows, nt the number of activation rows ("tokens"). Shape limits:
  *    1 <= N <= Q6K_MAX_N, 1 <= nt <= Q6K_MAX_NT, 0 < K <= Q6K_MAX_K, and K a

@@ -2,8 +2,10 @@
 //
 // Each entry point validates every argument (shape, NULL, 16-byte alignment,
 // output/input overlap) before queuing anything, then queues its kernels on the
-// caller's stream and returns. No entry point allocates, synchronises or caches
-// data; the only process-wide state is a per-device table of compute-unit counts.
+// caller's stream and returns. No entry point allocates, synchronises or keeps data
+// of a call. Process-wide state: the per-device table of compute-unit counts below,
+// and the per-device, per-kernel occupancy table of the launchers (wg_fit in
+// mmvq.hip); both are filled on first use and kept until the process ends.
 
 #include <atomic>
 

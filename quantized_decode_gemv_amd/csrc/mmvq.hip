@@ -42,6 +42,7 @@
 
 #include <map>
 #include <mutex>
+#include <tuple>
 #include <unordered_map>
 
 #include "kq_unit.h"
@@ -205,16 +206,6 @@ __device__ __forceinline__ void lane_acts(LaneState<F, NT, CPL, ACT_REGS> &st, c
                 F::drop(st.act[i][t]);
         }
     }
-}
-
-template <class F, int NT, int CPL, int AM>
-__device__ __forceinline__ void lane_init(LaneState<F, NT, CPL, AM> &st, uint32_t lane,
-                                          uint32_t nbe, const int8_t *qs, const uint16_t *d8,
-                                          uint32_t K)
-{
-    lane_chunks(st, lane, nbe);
-    if constexpr (AM == ACT_REGS)
-        lane_acts(st, qs, d8, K);
 }
 
 template <class F, int NT, int CPL, int AM>
@@ -464,7 +455,13 @@ __global__ __launch_bounds__(WG) void mmvq_rows(const uint8_t *__restrict__ w,
         if (wave >= N)
             return;
     } else {
-        lane_init(st, lane, nbe, qs, d8, K);
+        // the activation operands first: with the weight rows requested before them,
+        // waiting for the operands (issued later) waits for the rows too, and the
+        // compiler's wait counts at the row loop's head then cover the look-ahead rows
+        // as well (measured slower on every shape it changed)
+        lane_chunks(st, lane, nbe);
+        if constexpr (AM == ACT_REGS)
+            lane_acts(st, qs, d8, K);
         if (wave >= N)
             return;
         prime_rows<F, NT, CPL, 0, DEPTH - 1, AM>(bufs, w, wave, nw, N, stride, st);
@@ -807,7 +804,8 @@ __global__ __launch_bounds__(WG) void gate_up_swiglu_rows(
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     LaneState<F, 1, CPL, ACT_REGS> st;
-    lane_init(st, lane, nbe, qs, d8, K);
+    lane_chunks(st, lane, nbe);
+    lane_acts(st, qs, d8, K);
     const uint32_t N = 2u * Nh, nblk = Nh / 32u;
     typename F::W A[CPL], B[CPL];
     for (uint32_t b = blockIdx.x; b < nblk; b += gridDim.x) {
@@ -860,7 +858,11 @@ __global__ __launch_bounds__(WG) void gate_up_swiglu_rows(
     }
 }
 
-// Any row length: a row is walked in steps of STEP chunks per lane.
+// Any row length: a row is walked in steps of STEP chunks per lane. Each step's
+// chunks are summed in f32 (at most STEP roundings) and the step sums are added in
+// f64, so a lane's rounding error does not grow with the row length (a row of 2^20
+// weights is 512 steps per lane); the lane total is rounded once to f32 before the
+// wave reduction.
 template <class F, int NT>
 __global__ __launch_bounds__(WG) void mmvq_long(const uint8_t *__restrict__ w,
                                                 const int8_t *__restrict__ qs,
@@ -875,10 +877,10 @@ __global__ __launch_bounds__(WG) void mmvq_long(const uint8_t *__restrict__ w,
     const uint32_t C = 8u * nbe;
     for (uint32_t row = wave; row < N; row += nw) {
         const __amdgpu_buffer_rsrc_t r = row_desc(w, row, stride);
-        float acc[NT];
+        double lane_sum[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-            acc[t] = 0.0f;
+            lane_sum[t] = 0.0;
         for (uint32_t base = 0; base < C; base += 64u * STEP) {
             typename F::W wt[STEP];
             uint32_t Qs[STEP];
@@ -891,6 +893,10 @@ __global__ __launch_bounds__(WG) void mmvq_long(const uint8_t *__restrict__ w,
                 wt[i] = F::load(r, F::offsets(Qs[i], nbe));
             }
             __builtin_amdgcn_sched_barrier(0);
+            float acc[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                acc[t] = 0.0f;
 #pragma unroll
             for (int i = 0; i < STEP; ++i) {
 #pragma unroll
@@ -900,7 +906,14 @@ __global__ __launch_bounds__(WG) void mmvq_long(const uint8_t *__restrict__ w,
                     acc[t] = F::accumulate(acc[t], wt[i], a, Qs[i], live[i]);
                 }
             }
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                lane_sum[t] += (double)acc[t];
         }
+        float acc[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            acc[t] = (float)lane_sum[t];
         const float s = reduce_tokens<NT>(acc, lane);
         uint32_t t;
         if (stores_token<NT>(lane, t))
@@ -1053,17 +1066,22 @@ struct GemvArgs {
 };
 
 // Workgroups of `kern` that fit on one CU at once (its registers and LDS), from the
-// runtime's occupancy calculator, cached per kernel. Some long-row kernels need more
-// than the 256 registers per lane that two workgroups per CU leave; a grid sized
-// for two would then run in two rounds.
+// runtime's occupancy calculator. Some long-row kernels need more than the 256
+// registers per lane that two workgroups per CU leave; a grid sized for two would
+// then run in two rounds.
 // lds: the launch's dynamic LDS bytes (the kernel's own static LDS is known to the
 // runtime); past 64 KB the kernel is first allowed that much.
+// Process-wide state: the answer is kept per (current device, kernel, lds) for the
+// life of the process, behind a mutex, so the query runs once per kernel and size.
 int wg_fit(const void *kern, uint32_t lds = 0)
 {
     static std::mutex mu;
-    static std::map<std::pair<const void *, uint32_t>, int> cache;
+    static std::map<std::tuple<int, const void *, uint32_t>, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 0;
     std::lock_guard<std::mutex> lock(mu);
-    const auto key = std::make_pair(kern, lds);
+    const auto key = std::make_tuple(dev, kern, lds);
     auto it = cache.find(key);
     if (it != cache.end())
         return it->second;
