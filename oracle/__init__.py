@@ -188,7 +188,8 @@ def rmsnorm(x, gamma, eps: float) -> np.ndarray:
 
 
 def swiglu(g, u) -> np.ndarray:
-    """g, u float32 [nt, K] -> y = silu(g) * u float32 [nt, K] (exact, rounded once)."""
+    """g, u float32 [nt, K] -> y = silu(g) * u float32 [nt, K] (evaluated in fp64, then
+    rounded to f32: within an ulp of the exactly rounded value)."""
     g = np.ascontiguousarray(np.atleast_2d(g), dtype=np.float32)
     u = np.ascontiguousarray(np.atleast_2d(u), dtype=np.float32)
     assert g.shape == u.shape

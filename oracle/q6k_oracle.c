@@ -19,9 +19,11 @@
  *   [D3-5] "70 · D3-5 -- decode-alignment plan Stage 1: fused-producer decode
  *           A-quantize"
  *
- * The SwiGLU producer (orc_swiglu) is the plain definition silu(g) * u, computed in
- * fp64 and rounded once to f32; the pages' f32 body rounds at each step, so the
- * HIP producer is compared to it within a few ulp (its last bits are not pinned).
+ * The SwiGLU producer (orc_swiglu) is the plain definition silu(g) * u evaluated in
+ * fp64 (libm exp, then three fp64 operations, each relative error ~2^-53) and rounded
+ * to f32 at the end: within an f32 ulp of the exactly rounded value, not always equal
+ * to it. The pages' f32 body rounds at each step, so the HIP producer is compared to
+ * it within a few ulp (its last bits are not pinned).
  *
  * Parity pins (tests/test_oracle_*.py): every function here is pinned by something
  * other than itself -- hand-worked addressing fixtures, closed forms, exact
@@ -338,8 +340,10 @@ int orc_rmsnorm(const float *x, const float *gamma, float eps, int64_t K, int nt
 }
 
 /* SwiGLU of nt rows of K gate/up pairs: y = silu(g) * u = g / (1 + e^-g) * u
- * ([D3-5] §3.2, the fused swiglu producer's body), the exact value rounded once
- * to f32 (evaluated in fp64). */
+ * ([D3-5] §3.2, the fused swiglu producer's body), evaluated in fp64 (libm exp) and
+ * rounded to f32 once at the end; the fp64 evaluation's own error (a few 2^-53
+ * relative) can move the f32 result by one ulp where the value lies near a rounding
+ * boundary. */
 int orc_swiglu(const float *g, const float *u, int64_t K, int nt, float *y)
 {
     if (K <= 0 || nt < 1)
