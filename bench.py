@@ -62,7 +62,8 @@ PROBE_FORMS = {0: "buffer_nt", 1: "buffer_default", 2: "global_nt", 3: "global_d
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mmvq_lm_head_traffic.txt")
 TYPE_NAMES = {12: "q4_K", 13: "q5_K", 14: "q6_K"}
 # the GEMV kernel by the plan's kind
-GEMV_KERNELS = {0: "mmvq_long", 1: "mmvq_rows", 2: "mmvq_split", 3: "mmvq_pairs"}
+GEMV_KERNELS = {0: "mmvq_long", 1: "mmvq_rows", 2: "mmvq_split", 3: "mmvq_pairs",
+                4: "mmvq_pairs_ring"}
 PRODUCER_NAMES = {"rmsnorm": "fused RMSNorm->q8", "swiglu": "fused SwiGLU->q8",
                   "quant": "q8"}
 KERNEL_SOURCES = [os.path.join(ROOT, "quantized_decode_gemv_amd", "csrc", f)

@@ -61,3 +61,32 @@ __device__ __forceinline__ uint32_t load_b16(__amdgpu_buffer_rsrc_t r, uint32_t 
 }
 
 }  // namespace q6k
+
+namespace q6k {
+
+// One wave instruction that copies 16 bytes per lane, from buffer offset voff + soff,
+// into LDS at lds + 16 * lane (a buffer load whose destination is LDS, non-temporal
+// like the streamed planes). The LDS base travels in M0, which the compiler loads
+// for the statement. The compiler does not count this load: a caller waits for it
+// with vm_wait before reading the bytes from LDS, and issues no LDS reads of the
+// destination that could be served before it.
+__device__ __forceinline__ void dma_b128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                         uint32_t lds)
+{
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen nt lds"
+                 :
+                 : "v"(voff), "s"(r), "s"(soff), "{m0}"(lds)
+                 : "memory");
+}
+
+// Waits until at most N vector memory instructions of this wave are outstanding.
+// Loads complete in issue order, so after the wait every load issued before the
+// last N vector memory instructions has completed (stores only add to the count).
+template <int N>
+__device__ __forceinline__ void vm_wait()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+}  // namespace q6k

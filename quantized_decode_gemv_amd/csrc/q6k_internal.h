@@ -17,10 +17,11 @@ struct MmvqPlan {
     bool shared = false;    // the rows shared by a workgroup's four waves (cpl is then
                             // per thread of the 256)
     bool paired = false;    // two rows per wave, the last chunk slot split between them
+    bool ring = false;      // paired, the pairs' bytes streamed through an LDS ring
     int act_mode = 0;       // activation operands across rows: 0 re-read per row,
                             // 1 registers, 2 staged in LDS once per workgroup
     int launches = 0;       // one launch per group of up to 4 token columns
-    int depth = 1;          // rows in flight per wave
+    int depth = 1;          // rows (paired: pairs) in flight per wave
 };
 
 MmvqPlan plan_mmvq(int type, int64_t N, int64_t K, int nt, int num_cu);

@@ -161,7 +161,7 @@ def test_plan_covers_every_row_length(nbe, nt):
     assert p["unrolled"] == (8 * nbe <= 12 * 64)
     assert p["launches"] == -(-nt // 4)
     assert p["act_mode"] in (0, 1, 2)
-    assert p["grid"] >= 1 and p["depth"] in (1, 2, 3)
+    assert p["grid"] >= 1 and p["depth"] in ((1, 2, 3, 4) if p["ring"] else (1, 2, 3))
 
 
 @pytest.mark.parametrize("qtype", [14, 12, 13])
@@ -203,10 +203,14 @@ def test_plan_pairs_rule(qtype, nbe, nt, N):
     expect = (min(nt, 4) >= 2 and (8 * nbe) % 64 == 32 and -(-8 * nbe // 64) <= 3
               and (N + 1) // 2 >= 2048)
     assert p["paired"] == expect
+    # the pairs of q6_K rows of 20 super-blocks at 4 tokens stream through an LDS ring,
+    # four pairs deep
+    ring = expect and qtype == 14 and min(nt, 4) == 4 and nbe == 20
+    assert p["ring"] == ring
     if expect:
         pairs = (N + 1) // 2
         assert p["cpl"] == -(-8 * nbe // 64) and p["grid"] == min(-(-pairs // 4), 256)
-        assert p["depth"] == 2 and p["act_mode"] == 1
+        assert p["depth"] == (4 if ring else 2) and p["act_mode"] == 1
 
 
 @pytest.mark.parametrize("N", [1, 2, 3, 63, 64, 65, 1023, 1024, 1025, 4096, 152064])
