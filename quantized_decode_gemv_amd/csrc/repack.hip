@@ -6,9 +6,9 @@
 // [0,128) to the ql plane at b*128, [128,192) to the qh plane at nbe*128 + b*64,
 // [192,208) to the sc plane at nbe*192 + b*16, [208,210) to the d plane at
 // nbe*208 + b*2); the row tail up to the 16-byte stride is zero.
-// The device kernel writes one 32-bit word of the split-plane row per thread,
-// gathering its four source bytes, so every output byte (pad included) is written
-// exactly once.
+// The device kernel takes one row per workgroup and writes each 32-bit word of the
+// split-plane row once (pad included), reading its source bytes as one word or two
+// 16-bit halves of the raw block.
 
 #include <string.h>
 
@@ -19,36 +19,74 @@ namespace q6k {
 
 namespace {
 
-// Raw source byte of split-plane row byte o (0 for the tail pad).
-__device__ __forceinline__ uint32_t src_byte(const uint8_t *__restrict__ raw_row, uint32_t o,
-                                             uint32_t nbe, const PlaneMap &m)
+// Bytes [0, n) of src as a little-endian word: as one word (ALIGN 4), two 16-bit
+// halves (ALIGN 2) or single bytes (ALIGN 1, any address).
+template <int ALIGN>
+__device__ __forceinline__ uint32_t read_le(const uint8_t *src, uint32_t n)
 {
-    uint32_t base = 0;
+    if constexpr (ALIGN == 4) {
+        return *reinterpret_cast<const uint32_t *>(src);
+    } else if constexpr (ALIGN == 2) {
+        const uint16_t *h = reinterpret_cast<const uint16_t *>(src);
+        return (uint32_t)h[0] | (n > 2u ? (uint32_t)h[1] << 16 : 0u);
+    } else {
+        uint32_t v = 0;
+        for (uint32_t k = 0; k < n; ++k)
+            v |= (uint32_t)src[k] << (8u * k);
+        return v;
+    }
+}
+
+// One 32-bit word of a split-plane row: bytes [o, o + 4) of the row at raw_row.
+// Plane starts (nbe times the sizes of the planes before) are multiples of 4, as are
+// the field sizes but q6_K's 2-byte d, so a word holds 4 bytes of one block's field
+// or (d) the fields of blocks b and b + 1; bytes past the row's raw length are the
+// zero pad. ALIGN: the alignment the raw rows guarantee for each field read (q6_K
+// blocks of 210 B give 2 on an even base, q4_K / q5_K blocks of 144 / 176 B give 4
+// on a base that is a multiple of 4; 1 for any other base).
+template <int TYPE, int ALIGN>
+__device__ __forceinline__ uint32_t dpl_word(const uint8_t *__restrict__ raw_row, uint32_t o,
+                                             uint32_t nbe)
+{
+    constexpr PlaneMap m = plane_map(TYPE);
+    uint32_t start = 0;
+#pragma unroll
     for (uint32_t p = 0; p < m.n; ++p) {
         const uint32_t len = m.size[p] * nbe;
-        if (o < base + len) {
-            const uint32_t r = o - base;
-            return raw_row[(size_t)(r / m.size[p]) * m.block + m.off[p] + r % m.size[p]];
+        if (o < start + len) {
+            const uint32_t r = o - start;
+            const uint32_t b = r / m.size[p], within = r - b * m.size[p];
+            const uint8_t *src = raw_row + (size_t)b * m.block + m.off[p] + within;
+            if (m.size[p] == 2u) {   // d of blocks b and b + 1 (the pad past the last)
+                const uint32_t hi = b + 1u < nbe ? read_le<ALIGN>(src + m.block, 2u) : 0u;
+                return read_le<ALIGN>(src, 2u) | (hi << 16);
+            }
+            return read_le<ALIGN>(src, 4u);
         }
-        base += len;
+        start += len;
     }
     return 0u;
 }
 
+// One workgroup per row; the threads walk its words.
+template <int TYPE, int ALIGN>
 __global__ __launch_bounds__(256) void repack_kernel(const uint8_t *__restrict__ raw,
-                                                     uint32_t *__restrict__ dpl, uint64_t words,
-                                                     uint32_t nbe, uint32_t stride, PlaneMap m)
+                                                     uint32_t *__restrict__ dpl, uint32_t nbe,
+                                                     uint32_t stride)
 {
-    const uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x;
-    if (i >= words)
-        return;
-    const uint32_t wpr = stride / 4u;
-    const uint64_t row = i / wpr;
-    const uint32_t o = (uint32_t)(i % wpr) * 4u;
-    const uint8_t *src = raw + row * (uint64_t)(m.block * nbe);
-    const uint32_t v = src_byte(src, o, nbe, m) | (src_byte(src, o + 1, nbe, m) << 8) |
-                       (src_byte(src, o + 2, nbe, m) << 16) | (src_byte(src, o + 3, nbe, m) << 24);
-    dpl[i] = v;
+    const uint64_t row = blockIdx.x;
+    const uint8_t *src = raw + row * ((uint64_t)plane_map(TYPE).block * nbe);
+    uint32_t *dst = dpl + row * (stride / 4u);
+    for (uint32_t i = threadIdx.x; i < stride / 4u; i += 256u)
+        dst[i] = dpl_word<TYPE, ALIGN>(src, 4u * i, nbe);
+}
+
+template <int TYPE>
+const void *repack_kernel_for(const void *raw)
+{
+    constexpr int A = TYPE == KQT_Q6_K ? 2 : 4;
+    return (uintptr_t)raw % A == 0 ? (const void *)repack_kernel<TYPE, A>
+                                   : (const void *)repack_kernel<TYPE, 1>;
 }
 
 }  // namespace
@@ -58,16 +96,14 @@ hipError_t launch_repack(int type, const uint8_t *raw, uint8_t *dpl, int64_t N, 
 {
     uint32_t nbe = (uint32_t)(K / 256);
     uint32_t stride = (uint32_t)kq_row_stride(type, nbe);
-    uint64_t words = (uint64_t)N * stride / 4u;
     uint32_t *out = reinterpret_cast<uint32_t *>(dpl);
-    PlaneMap m = plane_map(type);
-    const uint64_t grid = (words + 255u) / 256u;
-    if (grid > 0x7FFFFFFFull)
+    if (N > 0x7FFFFFFF)
         return hipErrorInvalidValue;
-    void *args[] = {(void *)&raw, (void *)&out, (void *)&words, (void *)&nbe, (void *)&stride,
-                    (void *)&m};
-    return hipLaunchKernel((const void *)repack_kernel, dim3((uint32_t)grid), dim3(256), args, 0,
-                           s);
+    const void *kern = type == KQT_Q6_K   ? repack_kernel_for<KQT_Q6_K>(raw)
+                       : type == KQT_Q5_K ? repack_kernel_for<KQT_Q5_K>(raw)
+                                          : repack_kernel_for<KQT_Q4_K>(raw);
+    void *args[] = {(void *)&raw, (void *)&out, (void *)&nbe, (void *)&stride};
+    return hipLaunchKernel(kern, dim3((uint32_t)N), dim3(256), args, 0, s);
 }
 
 void repack_host(int type, const uint8_t *raw, uint8_t *dpl, int64_t N, int64_t K)

@@ -47,6 +47,25 @@ def test_device_repack_byte_exact(qtype, N, K):
     assert np.array_equal(dpl.cpu().numpy(), oracle.kq_repack_dpl(qtype, raw, N, K))
 
 
+# The raw matrix may start at any address: word reads where its base allows them,
+# byte reads otherwise (q6_K: 16-bit reads on an even base).
+@pytest.mark.parametrize("qtype", [q.KQ_Q4_K, q.KQ_Q5_K, q.KQ_Q6_K])
+@pytest.mark.parametrize("shift", [0, 1, 2, 3])
+def test_device_repack_any_raw_alignment(qtype, shift):
+    N, K = 5, 256 * 7
+    raw = (q6ksynth.raw_q6k(N, K, seed=9 + shift) if qtype == q.KQ_Q6_K
+           else q6ksynth.raw_kq(qtype, N, K, seed=9 + shift))
+    flat = torch.from_numpy(raw.reshape(-1)).to(DEV)
+    buf = torch.zeros(flat.numel() + 16, dtype=torch.uint8, device=DEV)
+    buf[shift:shift + flat.numel()] = flat
+    dpl = torch.full((q.kq_dpl_bytes(qtype, N, K),), 0xEE, dtype=torch.uint8, device=DEV)
+    q.repack_kq_dpl(qtype, buf[shift:shift + flat.numel()], dpl, N, K)
+    torch.cuda.synchronize()
+    expect = (oracle.repack_dpl(raw, N, K) if qtype == q.KQ_Q6_K
+              else oracle.kq_repack_dpl(qtype, raw, N, K))
+    assert np.array_equal(dpl.cpu().numpy(), expect)
+
+
 @pytest.mark.parametrize("qtype", TYPES, ids=_ids)
 @pytest.mark.parametrize("N,K,nt", [(64, 1024, 1), (37, 5120, 2), (5, 13824, 3),
                                     (3, 256 * 97, 1), (2, 256 * 200, 5)])
