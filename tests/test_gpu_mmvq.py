@@ -135,12 +135,16 @@ def test_shared_rows_random(N, nbe, nt):
 
 # Two rows per wave (2..4 tokens, rows of an odd multiple of 32 chunks: nbe 4, 12, 20):
 # every chunk count per lane 1..3, an odd N (the last pair has one row), and nt = 5 (a
-# paired launch of 4 tokens, then a one-wave launch of 1).
+# paired launch of 4 tokens, then a one-wave launch of 1). At 4 tokens and nbe 20 the
+# pairs stream through the LDS ring: 4095 and 4097 rows give every wave two pairs, and
+# one wave a third whose second row is past the end.
 @pytest.mark.parametrize("nbe", [4, 12, 20])
-@pytest.mark.parametrize("N,nt", [(4095, 2), (4097, 3), (8192, 4), (4099, 5)])
+@pytest.mark.parametrize("N,nt", [(4095, 2), (4097, 3), (8192, 4), (4099, 5), (4095, 4),
+                                  (4097, 4)])
 def test_pairs_random(nbe, N, nt):
     K = 256 * nbe
-    assert q.mmvq_plan(N, K, nt, 256)["paired"]
+    plan = q.mmvq_plan(N, K, nt, 256)
+    assert plan["paired"] and plan["ring"] == (nbe == 20 and nt >= 4)
     raw = q6ksynth.raw_q6k(N, K, seed=N * 3 + nbe + nt)
     dpl = dpl_from_raw(raw, N, K)
     x = np.stack([q6ksynth.activation("outlier", K, 1400 + c) for c in range(nt)])
