@@ -26,7 +26,9 @@
 //    branch-free and their waits are counted exactly;
 //  - DEPTH rows are in flight per wave: the next rows' loads are issued before the
 //    current row's arithmetic (scheduling barriers keep the compiler from sinking
-//    them), so a wave never idles with nothing requested;
+//    them), so a wave never idles with nothing requested; where the weight buffers
+//    would crowd the registers (row pairs at 4 tokens, lm_head width), rows are
+//    instead copied into a per-wave ring in LDS ahead of use (mmvq_pairs_ring);
 //  - a lane's activation operands are the same for every row; they stay in
 //    registers (ACT_REGS) when they fit next to the weight buffers, else the
 //    workgroup stages them once in LDS and reads them per row (ACT_LDS; the
