@@ -183,7 +183,7 @@ __device__ __forceinline__ float4 rms_scale(float4 x, float4 g, float r)
 // gamma (zeros past K/4). Calls put(t, f, y, q8) for every live float4 index f
 // (q8.d16 is the scale of block f / 8). Every thread must call it; part holds
 // NORM_WG / 64 doubles of LDS per token.
-template <int NT, int VPT, typename Put>
+template <int NT, int VPT, bool SKIP_PAST = false, typename Put>
 __device__ __forceinline__ void norm_quant_rows(const float4 (&xv)[NT][VPT],
                                                 const float4 (&gv)[VPT], uint32_t K, float eps,
                                                 double *part, Put &&put)
@@ -192,12 +192,18 @@ __device__ __forceinline__ void norm_quant_rows(const float4 (&xv)[NT][VPT],
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         double acc = 0.0;
+        // SKIP_PAST: a group v with v * NORM_WG >= K4 holds only the zeros past the
+        // row (each would add +0) and no output, so the whole workgroup skips it; the
+        // results are the same either way
 #pragma unroll
         for (int v = 0; v < VPT; ++v)
-            acc = sq_chain4(acc, xv[t][v]);
+            if (!SKIP_PAST || (uint32_t)v * NORM_WG < K4)
+                acc = sq_chain4(acc, xv[t][v]);
         const float r = norm_factor(norm_block_total(acc, part + t * (NORM_WG / 64)), K, eps);
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
+            if (SKIP_PAST && (uint32_t)v * NORM_WG >= K4)
+                break;
             const uint32_t f = threadIdx.x + v * NORM_WG;
             const float4 yv = rms_scale(xv[t][v], gv[v], r);
             const Q8Out o = quant_group8(yv);
