@@ -63,12 +63,12 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mmvq_lm_head_traffic.txt")
 TYPE_NAMES = {12: "q4_K", 13: "q5_K", 14: "q6_K"}
 # the GEMV kernel by the plan's kind
 GEMV_KERNELS = {0: "mmvq_long", 1: "mmvq_rows", 2: "mmvq_split", 3: "mmvq_pairs",
-                4: "mmvq_pairs_ring"}
+                4: "mmvq_tiles"}
 PRODUCER_NAMES = {"rmsnorm": "fused RMSNorm->q8", "swiglu": "fused SwiGLU->q8",
                   "quant": "q8"}
 KERNEL_SOURCES = [os.path.join(ROOT, "quantized_decode_gemv_amd", "csrc", f)
-                  for f in ("mmvq.hip", "q6k_unit.h", "q6k_norm.h", "kq_unit.h", "kq_format.h",
-                            "bufload.h")]
+                  for f in ("mmvq.hip", "tiles.hip", "q6k_unit.h", "q6k_norm.h", "kq_unit.h",
+                            "kq_format.h", "bufload.h")]
 
 
 def log(*a):

@@ -267,12 +267,14 @@ int mmvq_kq_q8_subdots(int type, const void *w_dpl, const void *q8, int32_t *dot
  *   3 a fixed-length kernel with two rows per wave (2..4 tokens, K = 1024, 3072 or
  *     5120, whose rows hold an odd multiple of 32 chunks, and at least 4 rows per wave
  *     of its grid); each half of the wave takes one row's last chunk slot;
- *   4 kind 3 with each pair's bytes copied into a ring in LDS ahead of its use (q6_K,
- *     4 tokens, K = 5120); same results as kind 3;
+ *   4 16-row tiles on the int8 matrix cores (q6_K, 3 or 4 tokens, K = 5120, N >= 16):
+ *     a workgroup's four waves copy 16 consecutive rows into LDS and each takes a
+ *     quarter of K; each output adds the four quarters in a fixed order;
  * out6[3] = where activation operands live across rows (0: re-read from the q8
  *   plane per row, 1: registers, 2: staged once per workgroup in LDS);
  * out6[4] = launches (one per group of up to 4 token columns);
- * out6[5] = rows (kinds 3 and 4: row pairs) in flight per wave.
+ * out6[5] = rows (kind 3: row pairs) in flight per wave; kind 4: tile buffers per
+ *   workgroup.
  * The kernel fields describe the first launch. Host only. */
 int q6k_mmvq_plan(int64_t N, int64_t K, int nt, int num_cu, int32_t *out6);
 

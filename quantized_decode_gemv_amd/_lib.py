@@ -233,10 +233,9 @@ def mmvq_plan(N: int, K: int, nt: int, num_cu: int, qtype: int = 14) -> dict:
     # 2 staged in LDS once per workgroup
     # kind: 0 generic stepping kernel, 1 one wave per row, 2 rows shared by the
     # workgroup's four waves (cpl then counts chunks per thread of the 256), 3 two rows
-    # per wave sharing the last chunk slot, 4 as 3 with the pairs' bytes copied through
-    # an LDS ring
+    # per wave sharing the last chunk slot, 4 16-row tiles on the int8 matrix cores
     return dict(grid=out[0], cpl=out[1], unrolled=out[2] >= 1, shared=out[2] == 2,
-                paired=out[2] in (3, 4), ring=out[2] == 4, kind=out[2], hoist=out[3] == 1,
+                paired=out[2] == 3, tiles=out[2] == 4, kind=out[2], hoist=out[3] == 1,
                 act_mode=out[3], launches=out[4], depth=out[5])
 
 

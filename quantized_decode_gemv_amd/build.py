@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libq6kdpl.so")
-SOURCES = ["abi.hip", "mmvq.hip", "producer.hip", "repack.hip"]
+SOURCES = ["abi.hip", "mmvq.hip", "producer.hip", "repack.hip", "tiles.hip"]
 # the read-bandwidth probe of the measurement harness (bench.py --read-ceiling), a
 # library of its own so the GEMV library holds only the path
 PROBE_LIB = os.path.join(PKG, "libq6kprobe.so")

@@ -388,7 +388,7 @@ int kq_mmvq_plan(int type, int64_t N, int64_t K, int nt, int num_cu, int32_t *ou
     const q6k::MmvqPlan p = q6k::plan_mmvq(type, N, K, nt, num_cu);
     out6[0] = (int32_t)p.grid;
     out6[1] = p.cpl;
-    out6[2] = p.ring ? 4 : p.paired ? 3 : p.shared ? 2 : p.unrolled ? 1 : 0;
+    out6[2] = p.tiles ? 4 : p.paired ? 3 : p.shared ? 2 : p.unrolled ? 1 : 0;
     out6[3] = p.act_mode;
     out6[4] = p.launches;
     out6[5] = p.depth;

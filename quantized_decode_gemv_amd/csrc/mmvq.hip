@@ -26,9 +26,7 @@
 //    branch-free and their waits are counted exactly;
 //  - DEPTH rows are in flight per wave: the next rows' loads are issued before the
 //    current row's arithmetic (scheduling barriers keep the compiler from sinking
-//    them), so a wave never idles with nothing requested; where the weight buffers
-//    would crowd the registers (row pairs at 4 tokens, lm_head width), rows are
-//    instead copied into a per-wave ring in LDS ahead of use (mmvq_pairs_ring);
+//    them), so a wave never idles with nothing requested;
 //  - a lane's activation operands are the same for every row; they stay in
 //    registers (ACT_REGS) when they fit next to the weight buffers, else the
 //    workgroup stages them once in LDS and reads them per row (ACT_LDS; the
@@ -717,90 +715,6 @@ __global__ __launch_bounds__(WG) void mmvq_pairs(const uint8_t *__restrict__ w,
 }
 #undef PAIR_STEP
 
-// Row pairs whose bytes stream through LDS. A pair of rows is contiguous in the
-// matrix (2 * stride bytes), so each wave copies whole pairs into a ring of D slots
-// of its own with buffer-to-LDS loads (1 KB per instruction, no registers held while
-// in flight), D - 1 pairs ahead of the one it computes; the lanes then read their
-// chunks from LDS at the same offsets as mmvq_pairs and run its arithmetic, so the
-// outputs equal mmvq_pairs' bit for bit. Used for 4 tokens on q6_K rows of 20
-// super-blocks (lm_head width), where mmvq_pairs holds two pairs of weights in
-// registers next to its activation operands, runs past 256 registers and keeps
-// fewer bytes in flight. Per step the wave issues pair p + D - 1, waits for pair p
-// (vm_wait: every load issued before the last (D - 1) pairs' copies has landed) and
-// reads slot p % D; the slot it refills is the one read in the previous step, whose
-// reads were consumed there. The ring is unrolled D steps deep so each slot offset is
-// a constant.
-template <class F, int CPL>
-struct PairGeom {
-    static constexpr uint32_t NBE = 8u * (CPL - 1) + 4u;    // rows of 64 * (CPL - 1) + 32 chunks
-    static constexpr uint32_t STRIDE = (uint32_t)kq_row_stride(F::TYPE, NBE);
-    static constexpr uint32_t NLD = (2u * STRIDE + 1023u) / 1024u;   // copies per pair
-    static constexpr uint32_t SLOT = NLD * 1024u;
-};
-
-constexpr int RING_DEPTH = 4;
-
-template <class F, int NT, int CPL, int D>
-__global__ __launch_bounds__(WG) void mmvq_pairs_ring(const uint8_t *__restrict__ w,
-                                                      const int8_t *__restrict__ qs,
-                                                      const uint16_t *__restrict__ d8,
-                                                      float *__restrict__ y, uint32_t N,
-                                                      uint32_t nbe, uint32_t stride, uint32_t K,
-                                                      uint32_t ldy)
-{
-    using G = PairGeom<F, CPL>;
-    static_assert(D >= 2 && (D - 1) * (int)G::NLD <= 63, "ring depth");
-    __shared__ __align__(16) uint8_t ring[WAVES_PER_WG * D * G::SLOT];
-    const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t wave = blockIdx.x * WAVES_PER_WG + wv;
-    const uint32_t nw = gridDim.x * WAVES_PER_WG;
-    const uint32_t P = (N + 1u) / 2u;
-    PairState<F, NT, CPL> st;
-    pair_init(st, lane, nbe, stride, qs, d8, K);
-    if (wave >= P)
-        return;
-    uint8_t *mine = ring + wv * (D * G::SLOT);
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)mine;
-    // pair p into slot `slot`: rows 2p and 2p + 1 below N (past the end: an empty
-    // descriptor, whose copies write zeros without a memory request)
-    auto copy_pair = [&](uint32_t slot, uint32_t p) {
-        const uint32_t r0 = 2u * p;
-        const uint32_t rows = r0 < N ? (N - r0 < 2u ? N - r0 : 2u) : 0u;
-        const __amdgpu_buffer_rsrc_t r =
-            buf_desc(w + (size_t)(rows ? r0 : 0u) * stride, rows * stride);
-#pragma unroll
-        for (uint32_t j = 0; j < G::NLD; ++j)
-            dma_b128(r, 16u * lane, 1024u * j, lds0 + slot * G::SLOT + 1024u * j);
-    };
-#pragma unroll
-    for (int k = 0; k < D - 1; ++k)
-        copy_pair((uint32_t)k, wave + (uint32_t)k * nw);
-    uint32_t p = wave;
-    for (;;) {
-#pragma unroll
-        for (int k = 0; k < D; ++k) {
-            copy_pair((uint32_t)((k + D - 1) % D), p + (uint32_t)(D - 1) * nw);
-            vm_wait<(D - 1) * (int)G::NLD>();
-            const uint8_t *src = mine + k * G::SLOT;
-            PairBufs<F, CPL> b;
-#pragma unroll
-            for (int i = 0; i < CPL; ++i)
-                b.X[i] = F::load_lds(src, st.ox[i]);
-#pragma unroll
-            for (int i = 0; i < CPL - 1; ++i)
-                b.Y[i] = F::load_lds(src, st.oy[i]);
-            finish_pair<F, NT, CPL>(b, st, y, ldy, p, N, lane);
-            p += nw;
-            if (p >= P)
-                goto done;
-        }
-    }
-done:
-    // no copy may still be landing in LDS when the workgroup ends
-    vm_wait<0>();
-}
-
 // RMSNorm -> q8 -> GEMV in one kernel, for the shapes whose activation operands
 // stay in registers. Every workgroup normalizes and quantizes the NT activation
 // rows itself, into LDS, with the RMSNorm -> q8 producer's own body and order
@@ -1429,27 +1343,11 @@ bool pairs_ok(int type, int nt, int cpl, int64_t N, int64_t K, int num_cu)
     return (N + 1) / 2 >= 2 * waves;
 }
 
-// Row pairs through the LDS ring (mmvq_pairs_ring) for 4 tokens on q6_K rows of 20
-// super-blocks. Measured against mmvq_pairs (graph-replayed GEMV, one MI355X, five
-// interleaved runs): lm_head 152064 x 5120 at 4 tokens 104.1-108.2 -> 100.5-102.5 us;
-// at 2 and 3 tokens the ring measured 5 % slower (92.4 -> 97.4, 96.2 -> 101.3), and
-// on q4_K rows mixed (27648 x 5120 at 4 tokens 20.0 -> 21.2), so those keep
-// mmvq_pairs. One workgroup per CU (the rings take 144 KB of LDS).
-constexpr bool ring_ok(int type, int nt, int cpl)
-{
-    return type == KQT_Q6_K && nt == 4 && cpl == 3;
-}
-
 template <class F, int NT, int CPL>
 hipError_t launch_pairs(int num_cu, hipStream_t s, GemvArgs a)
 {
     constexpr RowsCfg k = pairs_cfg(F::TYPE, NT, CPL);
     const void *kern = (const void *)mmvq_pairs<F, NT, CPL, k.depth>;
-    if constexpr (ring_ok(F::TYPE, NT, CPL)) {
-        if (a.stride != PairGeom<F, CPL>::STRIDE)
-            return hipErrorInvalidValue;
-        kern = (const void *)mmvq_pairs_ring<F, NT, CPL, RING_DEPTH>;
-    }
     const int fit = wg_fit(kern);
     if (fit < 1)
         return hipErrorInvalidValue;
@@ -1491,7 +1389,9 @@ hipError_t launch_mmvq_fmt(const uint8_t *w, const uint8_t *q8, float *y, int64_
         a.K = (uint32_t)K;
         a.ldy = (uint32_t)N;
         hipError_t e;
-        if (pairs_ok(F::TYPE, n, cpl, N, K, num_cu)) {
+        if (tiles_ok(F::TYPE, N, K, n)) {
+            e = launch_tiles(w, a.qs, a.d8, a.y, N, a.ldy, n, num_cu, s);
+        } else if (pairs_ok(F::TYPE, n, cpl, N, K, num_cu)) {
             switch (n) {
             case 2: e = dispatch_pairs<F, 2>(cpl, num_cu, s, a); break;
             case 3: e = dispatch_pairs<F, 3>(cpl, num_cu, s, a); break;
@@ -1612,12 +1512,19 @@ MmvqPlan plan_mmvq(int type, int64_t N, int64_t K, int nt, int num_cu)
     p.unrolled = p.cpl <= MAX_CPL;
     p.launches = (nt + MAX_NT_KERNEL - 1) / MAX_NT_KERNEL;
     const int nt0 = nt < MAX_NT_KERNEL ? nt : MAX_NT_KERNEL;
+    if (tiles_ok(type, N, K, nt0)) {
+        p.tiles = true;
+        p.act_mode = ACT_REGS;
+        p.depth = 2;
+        const int64_t T = (N + 15) / 16;
+        p.grid = (uint32_t)(T < num_cu ? T : num_cu);
+        return p;
+    }
     if (pairs_ok(type, nt0, p.cpl, N, K, num_cu)) {
         p.paired = true;
-        p.ring = ring_ok(type, nt0, p.cpl);
         const RowsCfg c = pairs_cfg(type, nt0, p.cpl);
         p.act_mode = c.mode;
-        p.depth = p.ring ? RING_DEPTH : c.depth;
+        p.depth = c.depth;
         p.grid = grid_for((N + 1) / 2, num_cu, c.wg_per_cu);
         return p;
     }

@@ -17,15 +17,21 @@ struct MmvqPlan {
     bool shared = false;    // the rows shared by a workgroup's four waves (cpl is then
                             // per thread of the 256)
     bool paired = false;    // two rows per wave, the last chunk slot split between them
-    bool ring = false;      // paired, the pairs' bytes streamed through an LDS ring
+    bool tiles = false;     // 16-row tiles on the int8 matrix cores (tiles.hip)
     int act_mode = 0;       // activation operands across rows: 0 re-read per row,
                             // 1 registers, 2 staged in LDS once per workgroup
     int launches = 0;       // one launch per group of up to 4 token columns
-    int depth = 1;          // rows (paired: pairs) in flight per wave
+    int depth = 1;          // rows (paired: pairs) in flight per wave; tiles: tile
+                            // buffers per workgroup
 };
 
 MmvqPlan plan_mmvq(int type, int64_t N, int64_t K, int nt, int num_cu);
 
+// The q6_K GEMV at 3-4 tokens on 16-row tiles with the int8 matrix cores (tiles.hip):
+// rows of 20 super-blocks. qs, d8: the token group's q8 plane fields; y: [nt][ldy].
+bool tiles_ok(int type, int64_t N, int64_t K, int nt);
+hipError_t launch_tiles(const uint8_t *w, const int8_t *qs, const uint16_t *d8, float *y,
+                        int64_t N, int64_t ldy, int nt, int num_cu, hipStream_t s);
 // type: a KqType of kq_format.h (the weight rows are that type's split-plane rows).
 hipError_t launch_mmvq(int type, const uint8_t *w, const uint8_t *q8, float *y, int64_t N,
                        int64_t K, int nt, int num_cu, hipStream_t s);

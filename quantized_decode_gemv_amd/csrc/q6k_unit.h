@@ -217,17 +217,6 @@ struct FmtQ6K {
         return w;
     }
 
-    // The same fields from a copy of the row bytes in LDS (same offsets).
-    __device__ static W load_lds(const uint8_t *s, const Offs &o)
-    {
-        W w;
-        w.ql = *reinterpret_cast<const uint4 *>(s + o.ql);
-        w.qh = *reinterpret_cast<const uint4 *>(s + o.qh);
-        w.sc = *reinterpret_cast<const uint2 *>(s + o.sc);
-        w.d = *reinterpret_cast<const uint16_t *>(s + o.d);
-        return w;
-    }
-
     __device__ static Act act(const int8_t *qs_t, const uint16_t *d8_t, uint32_t Q)
     {
         return load_act(qs_t, d8_t, Q);

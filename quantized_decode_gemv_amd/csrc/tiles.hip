@@ -1,0 +1,275 @@
+// tiles.hip -- q6_K x q8 decode GEMV for 3-4 tokens on the int8 matrix cores
+// (gfx950 v_mfma_i32_16x16x64_i8), rows of 20 super-blocks (K = 5120, lm_head width).
+//
+// What is computed is the row kernels' sum (D4-2 §3.2 Excerpt C; D4-4 §3.2 Excerpt B):
+// y[t][r] = sum over the row's 16-element sub-blocks of d * sc * d8 * D, D the exact
+// int32 dot of (q - 32) with the token's int8 activations. Only the order of the float
+// additions differs from the row kernels.
+//
+// At several tokens the row kernels spend most of a wave's issue cycles on the dot
+// products and their conversions. Here one matrix instruction takes the integer dots
+// of 16 rows x 4 sub-blocks x 4 tokens:
+//  - B (64 x 16, one column per weight row): lane (r, g), g = lane / 16, holds 16 codes
+//    of row r, those of one sub-block; which sub-block the K-group g carries is fixed
+//    per step (below), the same for all 16 rows;
+//  - A (16 x 64, one row per (token t, sub-block slot s), row index 4s + t): the token's
+//    16 activations of slot s's sub-block in K-group s, zeros in the other K-groups;
+//  - C: -32 * (sum of those 16 activations), which folds the code offset in;
+//  - D = A * B + C, lane (r, g) receives rows 4g .. 4g + 3 of column r: the four tokens'
+//    exact sub-block dots of its own row and slot g, next to that row's scales.
+// The K order inside a K-group is whatever the instruction uses; A and B share it, and
+// a K-group holds one whole sub-block in both, so the result does not depend on it.
+//
+// Tiles of 16 consecutive rows are one contiguous run of 16 * stride bytes. A
+// workgroup's four waves copy a tile into LDS with buffer-to-LDS loads in 1 KB pieces
+// (contiguous requests, no registers held in flight; per-row runs of a few hundred
+// bytes measured markedly slower, as the row stride is not a multiple of the 128-byte
+// line) into one of two tile buffers, while they compute the other. Wave v computes
+// super-blocks 5v .. 5v + 4 of all 16 rows; the four partial sums of a row meet in
+// LDS and wave t adds them for token t and stores y. Its activation operands (A, C
+// and the q8 block scales) depend only on the wave's K quarter, so they are loaded
+// once and stay in registers for every tile. Per tile: two barriers (buffer free;
+// tile landed), each wave's own copies awaited with a counted wait (vm_wait), as
+// the compiler does not count buffer-to-LDS loads.
+//
+// Super-block sb of a row, lane K-group g = 2c + a (c the 128-element half, a the
+// 32-element unit inside it): the lane's 32 low-bit bytes (ql 128 sb + 32 g) hold
+// the codes of unit a (low nibbles) and unit a + 2 (high nibbles), positions 0..31;
+// their 2-bit fields are the 32 qh bytes at 64 sb + 32 c, fields 2a and 2a + 4. The
+// four steps of a super-block take, in K-group g: step 0 unit a positions 0..15,
+// step 1 positions 16..31, steps 2 and 3 the same of unit a + 2, i.e. sub-blocks
+// 8c + 2a + {0, 1, 4, 5}, whose scales are bytes 2a + {0, 1, 4, 5} of the 8-byte group
+// at 16 sb + 8c of the scale plane. Steps 0 and 1 lie in one q8 block (8 sb + 4c + a),
+// steps 2 and 3 in block + 2, so each pair's two scaled dots add exactly in int32
+// (|sc * D| < 2^23) before one conversion.
+
+#include "q6k_internal.h"
+#include "q6k_unit.h"
+
+namespace q6k {
+namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int TILE_WG = 256;     // four waves
+constexpr int TILE_WAVES = 4;
+constexpr uint32_t TILE_ROWS = 16;
+constexpr uint32_t TILE_NBE = 20;        // super-blocks per row (K = 5120)
+
+template <uint32_t NBE>
+struct TileGeom {
+    static constexpr uint32_t STRIDE = (uint32_t)kq_row_stride(KQT_Q6_K, NBE);
+    static constexpr uint32_t BYTES = TILE_ROWS * STRIDE;
+    static constexpr uint32_t RUNS = (BYTES + 4095u) / 4096u;   // 1 KB copies per wave per tile
+    static constexpr uint32_t BUF = TILE_WAVES * RUNS * 1024u;  // one tile buffer (copies past
+                                                                // the tile land zeros here)
+    static constexpr uint32_t SPW = NBE / TILE_WAVES;           // super-blocks per wave
+    static_assert(NBE % TILE_WAVES == 0, "whole K quarters");
+    static_assert(RUNS <= 63, "vmcnt range");
+};
+
+__device__ __forceinline__ uint32_t lds_offset(const void *p)
+{
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t *)p;
+}
+
+__device__ __forceinline__ i32x4 as_i32x4(uint4 v)
+{
+    i32x4 r;
+    r.x = (int)v.x;
+    r.y = (int)v.y;
+    r.z = (int)v.z;
+    r.w = (int)v.w;
+    return r;
+}
+
+template <int NT, uint32_t NBE>
+__global__ __launch_bounds__(TILE_WG) void mmvq_tiles(const uint8_t *__restrict__ w,
+                                                      const int8_t *__restrict__ qs,
+                                                      const uint16_t *__restrict__ d8,
+                                                      float *__restrict__ y, uint32_t N,
+                                                      uint32_t ldy)
+{
+    using G = TileGeom<NBE>;
+    constexpr uint32_t SPW = G::SPW;
+    constexpr uint32_t K = 256u * NBE;
+    __shared__ __align__(16) uint8_t tbuf[2 * G::BUF];
+    __shared__ float part[2][TILE_WAVES][4][TILE_ROWS];
+
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t r = lane & 15u, g = lane >> 4, c = g >> 1, a = g & 1u;
+    const uint32_t T = (N + TILE_ROWS - 1u) / TILE_ROWS;
+    if (blockIdx.x >= T)
+        return;
+    const uint32_t S = (T - 1u - blockIdx.x) / gridDim.x + 1u;   // this workgroup's tiles
+    const uint32_t lds0 = lds_offset(tbuf);
+
+    // tile s of this workgroup (blockIdx.x + s * gridDim.x) into buffer b: rows below
+    // N only (the copies of rows past N, and of a tile past the last, write zeros
+    // without a memory request)
+    auto copy_tile = [&](uint32_t b, uint32_t s) {
+        const uint32_t r0 = (blockIdx.x + s * gridDim.x) * TILE_ROWS;
+        const uint32_t rows = r0 < N ? (N - r0 < TILE_ROWS ? N - r0 : TILE_ROWS) : 0u;
+        const __amdgpu_buffer_rsrc_t rs =
+            buf_desc(w + (size_t)(rows ? r0 : 0u) * G::STRIDE, rows * G::STRIDE);
+#pragma unroll
+        for (uint32_t m = 0; m < G::RUNS; ++m) {
+            const uint32_t run = v + TILE_WAVES * m;
+            dma_b128(rs, 16u * lane, 1024u * run, lds0 + b * G::BUF + 1024u * run);
+        }
+    };
+    copy_tile(0, 0);
+
+    // the wave's activation operands, the same for every tile
+    i32x4 A[4 * SPW], C[4 * SPW];
+    float F[2 * SPW][NT];
+    {
+        const uint32_t ia = lane & 15u, ta = ia & 3u, sa = ia >> 2;
+        const bool live = sa == g && ta < (uint32_t)NT;
+        const __amdgpu_buffer_rsrc_t xr = buf_desc(qs, NT * K);
+        const uint32_t xbase = live ? ta * K : NT * K;   // past the extent: zeros
+#pragma unroll
+        for (uint32_t m = 0; m < SPW; ++m) {
+            const uint32_t sb = SPW * v + m;
+#pragma unroll
+            for (uint32_t j = 0; j < 4; ++j) {
+                const uint32_t off = 256u * sb + 128u * c + 32u * a + 64u * (j >> 1) + 16u * (j & 1u);
+                const uint4 x = load_b128<POLICY_DEFAULT>(xr, xbase + (live ? off : 0u));
+                A[4 * m + j] = as_i32x4(x);
+                const int ns = -32 * sum16_i8(x);
+                // lane (r, g) takes, for token t, the sum of A row 4g + t in K-group g:
+                // lane 16g + 4g + t
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    C[4 * m + j][t] = __builtin_amdgcn_ds_bpermute((int)(4u * (20u * g + t)), ns);
+            }
+#pragma unroll
+            for (uint32_t p = 0; p < 2; ++p) {
+                const uint32_t blk = 8u * sb + 4u * c + a + 2u * p;
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    F[2 * m + p][t] = f16_bits_to_f32(d8[(size_t)t * (K / 32u) + blk]);
+            }
+        }
+    }
+
+    const uint32_t sh = 2u * a, up = 4u - sh;
+    const uint32_t M = 0x33333333u << sh;
+    for (uint32_t s = 0; s < S; ++s) {
+        const uint32_t b = s & 1u;
+        __syncthreads();            // every wave is done with buffer b ^ 1 (tile s - 1)
+        copy_tile(b ^ 1u, s + 1u);
+        vm_wait<(int)G::RUNS>();    // this wave's copies of tile s have landed
+        __syncthreads();            // and every wave's
+        if (s > 0 && v < (uint32_t)NT && lane < TILE_ROWS) {
+            // tile s - 1: the four waves' partial sums of row `lane` for token v
+            const float(&pp)[TILE_WAVES][4][TILE_ROWS] = part[b ^ 1u];
+            const float tot = ((pp[0][v][lane] + pp[1][v][lane]) + pp[2][v][lane]) + pp[3][v][lane];
+            const uint32_t row = (blockIdx.x + (s - 1u) * gridDim.x) * TILE_ROWS + lane;
+            if (row < N)
+                y[(size_t)v * ldy + row] = tot;
+        }
+        const uint8_t *rb = tbuf + b * G::BUF + r * G::STRIDE;
+        float acc[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            acc[t] = 0.0f;
+#pragma unroll
+        for (uint32_t m = 0; m < SPW; ++m) {
+            const uint32_t sb = SPW * v + m;
+            const uint4 q0 = *reinterpret_cast<const uint4 *>(rb + 128u * sb + 32u * g);
+            const uint4 q1 = *reinterpret_cast<const uint4 *>(rb + 128u * sb + 32u * g + 16u);
+            const uint4 h0 = *reinterpret_cast<const uint4 *>(rb + 128u * NBE + 64u * sb + 32u * c);
+            const uint4 h1 = *reinterpret_cast<const uint4 *>(rb + 128u * NBE + 64u * sb + 32u * c + 16u);
+            const uint2 sc = *reinterpret_cast<const uint2 *>(rb + 192u * NBE + 16u * sb + 8u * c);
+            const uint32_t dbits = *reinterpret_cast<const uint16_t *>(rb + 208u * NBE + 2u * sb);
+            uint4 k0, k1, k2, k3;
+            uint32_t hm;
+            hm = h0.x & M; k0.x = codes_lo(q0.x, hm, up); k2.x = codes_hi(q0.x, hm, sh);
+            hm = h0.y & M; k0.y = codes_lo(q0.y, hm, up); k2.y = codes_hi(q0.y, hm, sh);
+            hm = h0.z & M; k0.z = codes_lo(q0.z, hm, up); k2.z = codes_hi(q0.z, hm, sh);
+            hm = h0.w & M; k0.w = codes_lo(q0.w, hm, up); k2.w = codes_hi(q0.w, hm, sh);
+            hm = h1.x & M; k1.x = codes_lo(q1.x, hm, up); k3.x = codes_hi(q1.x, hm, sh);
+            hm = h1.y & M; k1.y = codes_lo(q1.y, hm, up); k3.y = codes_hi(q1.y, hm, sh);
+            hm = h1.z & M; k1.z = codes_lo(q1.z, hm, up); k3.z = codes_hi(q1.z, hm, sh);
+            hm = h1.w & M; k1.w = codes_lo(q1.w, hm, up); k3.w = codes_hi(q1.w, hm, sh);
+            const i32x4 D0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[4 * m + 0], as_i32x4(k0), C[4 * m + 0], 0, 0, 0);
+            const i32x4 D1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[4 * m + 1], as_i32x4(k1), C[4 * m + 1], 0, 0, 0);
+            const i32x4 D2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[4 * m + 2], as_i32x4(k2), C[4 * m + 2], 0, 0, 0);
+            const i32x4 D3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[4 * m + 3], as_i32x4(k3), C[4 * m + 3], 0, 0, 0);
+            const int s0 = (int)(int8_t)(uint8_t)(sc.x >> (16u * a));
+            const int s1 = (int)(int8_t)(uint8_t)(sc.x >> (16u * a + 8u));
+            const int s2 = (int)(int8_t)(uint8_t)(sc.y >> (16u * a));
+            const int s3 = (int)(int8_t)(uint8_t)(sc.y >> (16u * a + 8u));
+            const float d = f16_bits_to_f32(dbits);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int i0 = __mul24(s0, D0[t]) + __mul24(s1, D1[t]);
+                const int i1 = __mul24(s2, D2[t]) + __mul24(s3, D3[t]);
+                acc[t] = __builtin_fmaf(d, (float)i0 * F[2 * m][t], acc[t]);
+                acc[t] = __builtin_fmaf(d, (float)i1 * F[2 * m + 1][t], acc[t]);
+            }
+        }
+        // row r's sum over the four K-groups (the same value in all four lanes), then
+        // lane (r, g) posts token g's
+        float mine = 0.0f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            float x = acc[t];
+            x += __shfl_xor(x, 32);
+            x += __shfl_xor(x, 16);
+            mine = g == (uint32_t)t ? x : mine;
+        }
+        part[b][v][g][r] = mine;
+    }
+    __syncthreads();
+    if (v < (uint32_t)NT && lane < TILE_ROWS) {
+        const float(&pp)[TILE_WAVES][4][TILE_ROWS] = part[(S - 1u) & 1u];
+        const float tot = ((pp[0][v][lane] + pp[1][v][lane]) + pp[2][v][lane]) + pp[3][v][lane];
+        const uint32_t row = (blockIdx.x + (S - 1u) * gridDim.x) * TILE_ROWS + lane;
+        if (row < N)
+            y[(size_t)v * ldy + row] = tot;
+    }
+    // no copy may still be landing in LDS when the workgroup ends
+    vm_wait<0>();
+}
+
+template <int NT>
+hipError_t launch_nt(const uint8_t *w, const int8_t *qs, const uint16_t *d8, float *y,
+                     uint32_t N, uint32_t ldy, int num_cu, hipStream_t s)
+{
+    const void *kern = (const void *)mmvq_tiles<NT, TILE_NBE>;
+    int fit = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&fit, kern, TILE_WG, 0) != hipSuccess ||
+        fit < 1)
+        return hipErrorInvalidValue;
+    const uint32_t T = (N + TILE_ROWS - 1u) / TILE_ROWS;
+    const uint32_t full = (uint32_t)num_cu * (uint32_t)fit;
+    const uint32_t grid = T < full ? T : full;
+    void *args[] = {(void *)&w, (void *)&qs, (void *)&d8, (void *)&y, (void *)&N, (void *)&ldy};
+    return hipLaunchKernel(kern, dim3(grid), dim3(TILE_WG), args, 0, s);
+}
+
+}  // namespace
+
+// Measured against the register row pairs (graph-replayed GEMV, lm_head 152064 x 5120,
+// one MI355X): 4 tokens 101.4 -> 97.9 us, 3 tokens 95.9 -> 95.1; at 2 tokens, where
+// the row pairs' arithmetic is light, 92.6 -> 94.8, so 2 tokens keep the row pairs.
+bool tiles_ok(int type, int64_t N, int64_t K, int nt)
+{
+    return type == KQT_Q6_K && K == 256 * (int64_t)TILE_NBE && nt >= 3 && nt <= 4 &&
+           N >= (int64_t)TILE_ROWS;
+}
+
+hipError_t launch_tiles(const uint8_t *w, const int8_t *qs, const uint16_t *d8, float *y,
+                        int64_t N, int64_t ldy, int nt, int num_cu, hipStream_t s)
+{
+    switch (nt) {
+    case 3: return launch_nt<3>(w, qs, d8, y, (uint32_t)N, (uint32_t)ldy, num_cu, s);
+    case 4: return launch_nt<4>(w, qs, d8, y, (uint32_t)N, (uint32_t)ldy, num_cu, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace q6k

@@ -161,7 +161,7 @@ def test_plan_covers_every_row_length(nbe, nt):
     assert p["unrolled"] == (8 * nbe <= 12 * 64)
     assert p["launches"] == -(-nt // 4)
     assert p["act_mode"] in (0, 1, 2)
-    assert p["grid"] >= 1 and p["depth"] in ((1, 2, 3, 4) if p["ring"] else (1, 2, 3))
+    assert p["grid"] >= 1 and p["depth"] in (1, 2, 3)
 
 
 @pytest.mark.parametrize("qtype", [14, 12, 13])
@@ -199,24 +199,33 @@ def test_plan_pairs_rule(qtype, nbe, nt, N):
     # two rows per wave at 2..4 tokens (per launch) when a row has an odd multiple of
     # 32 chunks, at most 3 chunks per lane, and at least two pairs per wave of the
     # grid (one workgroup per CU: 1024 waves on 256 CUs)
+    # q6_K rows of 20 super-blocks at 3 or 4 tokens take the matrix-core tiles instead
+    # (16 rows per tile, one workgroup per CU, two tile buffers)
     p = q.mmvq_plan(N, 256 * nbe, nt, 256, qtype)
+    tiles = qtype == 14 and nbe == 20 and min(nt, 4) >= 3 and N >= 16
+    assert p["tiles"] == tiles
+    if tiles:
+        assert not p["paired"] and p["grid"] == min(-(-N // 16), 256)
+        assert p["depth"] == 2 and p["act_mode"] == 1 and p["unrolled"]
+        return
     expect = (min(nt, 4) >= 2 and (8 * nbe) % 64 == 32 and -(-8 * nbe // 64) <= 3
               and (N + 1) // 2 >= 2048)
     assert p["paired"] == expect
-    # the pairs of q6_K rows of 20 super-blocks at 4 tokens stream through an LDS ring,
-    # four pairs deep
-    ring = expect and qtype == 14 and min(nt, 4) == 4 and nbe == 20
-    assert p["ring"] == ring
     if expect:
         pairs = (N + 1) // 2
         assert p["cpl"] == -(-8 * nbe // 64) and p["grid"] == min(-(-pairs // 4), 256)
-        assert p["depth"] == (4 if ring else 2) and p["act_mode"] == 1
+        assert p["depth"] == 2 and p["act_mode"] == 1
 
 
 @pytest.mark.parametrize("N", [1, 2, 3, 63, 64, 65, 1023, 1024, 1025, 4096, 152064])
 @pytest.mark.parametrize("nt", [1, 2, 4])
 def test_plan_grid_is_whole_cus_or_one_wave_per_row(N, nt):
     p = q.mmvq_plan(N, 5120, nt, 256)
+    # 16-row tiles at 4 tokens: one workgroup per tile up to one per CU
+    assert p["tiles"] == (nt == 4 and N >= 16)
+    if p["tiles"]:
+        assert p["grid"] == min(-(-N // 16), 256)
+        return
     # one wave per row, or per pair of rows (K = 5120 at several tokens, enough rows)
     assert p["paired"] == (nt >= 2 and (N + 1) // 2 >= 2 * 1024)
     units = -(-N // 2) if p["paired"] else N

@@ -120,16 +120,19 @@ def _gemv(qtype, W, qs, d16, N, K, nt):
     return y.cpu().numpy()
 
 
-# (N, K, nt) per GEMV kind: one wave per row at 1 and 3 chunks per lane; row pairs;
-# rows shared by a workgroup's waves; q6_K operands staged in LDS (11 chunks per lane,
-# enough rows for one wave per row); the generic long-row kernel
-SHAPES = [("rows-cpl1", 64, 1024, 1), ("rows-cpl3", 67, 5120, 3), ("pairs", 4099, 5120, 4),
+# (N, K, nt) per GEMV kind: one wave per row at 1 and 3 chunks per lane (q6_K: 15 rows,
+# below one tile); row pairs; rows shared by a workgroup's waves; q6_K operands staged
+# in LDS (11 chunks per lane, enough rows for one wave per row); the generic long-row
+# kernel; q6_K matrix-core tiles
+SHAPES = [("rows-cpl1", 64, 1024, 1), ("rows-cpl3", 15, 5120, 3), ("pairs", 4099, 5120, 2),
           ("shared", 2999, 18944, 1), ("shared-nt2", 1500, 13824, 2),
-          ("lds", 8192, 256 * 88, 1), ("long", 67, 256 * 100, 2)]
+          ("lds", 8192, 256 * 88, 1), ("long", 67, 256 * 100, 2), ("tiles", 4099, 5120, 4)]
 
 
-# (q4_K / q5_K long rows at one token are shared by a workgroup instead of staged)
-EDGE_CASES = [(t,) + s for t in (Q6, Q4, Q5) for s in SHAPES if t == Q6 or s[0] != "lds"]
+# (q4_K / q5_K long rows at one token are shared by a workgroup instead of staged; the
+# tiles are q6_K's)
+EDGE_CASES = [(t,) + s for t in (Q6, Q4, Q5) for s in SHAPES
+              if t == Q6 or s[0] not in ("lds", "tiles")]
 
 
 @pytest.mark.gpu
@@ -138,7 +141,8 @@ EDGE_CASES = [(t,) + s for t in (Q6, Q4, Q5) for s in SHAPES if t == Q6 or s[0] 
 def test_edge_gemv_every_kind(qtype, kind, N, K, nt):
     plan = q.mmvq_plan(N, K, nt, 256, qtype)
     say(f"edge {NAMES[qtype]} {kind} N={N} K={K} nt={nt}: plan {plan}")
-    expect = {"pairs": "paired", "shared": "shared", "shared-nt2": "shared"}.get(kind)
+    expect = {"pairs": "paired", "shared": "shared", "shared-nt2": "shared",
+              "tiles": "tiles"}.get(kind)
     if expect:
         assert plan[expect]
     if kind == "lds":

@@ -135,16 +135,15 @@ def test_shared_rows_random(N, nbe, nt):
 
 # Two rows per wave (2..4 tokens, rows of an odd multiple of 32 chunks: nbe 4, 12, 20):
 # every chunk count per lane 1..3, an odd N (the last pair has one row), and nt = 5 (a
-# paired launch of 4 tokens, then a one-wave launch of 1). At 4 tokens and nbe 20 the
-# pairs stream through the LDS ring: 4095 and 4097 rows give every wave two pairs, and
-# one wave a third whose second row is past the end.
+# paired launch of 4 tokens, then a one-wave launch of 1). At 3 and 4 tokens rows of 20
+# super-blocks take the matrix-core tiles instead (test_tiles_random).
 @pytest.mark.parametrize("nbe", [4, 12, 20])
 @pytest.mark.parametrize("N,nt", [(4095, 2), (4097, 3), (8192, 4), (4099, 5), (4095, 4),
                                   (4097, 4)])
 def test_pairs_random(nbe, N, nt):
     K = 256 * nbe
     plan = q.mmvq_plan(N, K, nt, 256)
-    assert plan["paired"] and plan["ring"] == (nbe == 20 and nt >= 4)
+    assert plan["paired"] == (nbe != 20 or nt == 2) and plan["tiles"] == (nbe == 20 and nt >= 3)
     raw = q6ksynth.raw_q6k(N, K, seed=N * 3 + nbe + nt)
     dpl = dpl_from_raw(raw, N, K)
     x = np.stack([q6ksynth.activation("outlier", K, 1400 + c) for c in range(nt)])
@@ -154,9 +153,31 @@ def test_pairs_random(nbe, N, nt):
     check_y(y, y_or, A, f"pairs N={N} nbe={nbe} nt={nt}")
 
 
+# 16-row tiles on the int8 matrix cores (q6_K, K = 5120, 3 or 4 tokens per launch):
+# a single tile, a ragged last tile (N % 16 = 1 and 15), fewer tiles than CUs, more
+# tiles than CUs with an uneven count per workgroup (4097 rows: 257 tiles, one
+# workgroup takes two), 5 and 7 tokens (a tile launch of 4, then 1 or 3 more), and
+# a zero activation row next to nonzero ones (its outputs must be exactly 0).
+@pytest.mark.parametrize("N,nt", [(16, 4), (17, 3), (31, 4), (100, 3), (4097, 4), (4111, 3),
+                                  (4096 * 3 + 5, 4), (1000, 5), (999, 7)])
+def test_tiles_random(N, nt):
+    K = 5120
+    plan = q.mmvq_plan(N, K, nt, 256)
+    assert plan["tiles"] and plan["grid"] == min(-(-N // 16), 256)
+    raw = q6ksynth.raw_q6k(N, K, seed=N * 5 + nt)
+    dpl = dpl_from_raw(raw, N, K)
+    x = np.stack([q6ksynth.activation("outlier", K, 1600 + c) for c in range(nt)])
+    x[1] = 0.0
+    qs, d = oracle.quant_q8(x)
+    y = run_mmvq(dpl, make_plane(qs, d), N, K, nt)
+    y_or, A = oracle.mmvq(oracle.RAW, raw, N, K, qs, d)
+    assert np.all(y[1] == 0)
+    check_y(y, y_or, A, f"tiles N={N} nt={nt}")
+
+
 # Matrices past 4 GiB of dpl rows: the rows past byte 2^32 need wider than 32-bit
 # offsets, in the repack and in the GEMV kinds that reach such sizes -- lm_head-width
-# rows (2^20 of them) at one token (one wave per row) and four (row pairs); tall-K
+# rows (2^20 of them) at one token (one wave per row) and four (matrix-core tiles); tall-K
 # rows at four tokens (operands staged in LDS); rows of 100 super-blocks (the generic
 # stepping kernel). The raw blocks are made on the device from a seeded generator
 # (uniform bytes, d = fp16(|N(0,1)| * 1e-3)); the oracle checks the first and last
