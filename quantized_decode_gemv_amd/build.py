@@ -26,6 +26,10 @@ HIPCC_FLAGS = [
     # no implicit multiply-add contraction: every fused multiply-add is written out,
     # so kernels that share arithmetic round identically
     "-ffp-contract=off",
+    # matrix-core instructions accumulate in ordinary vector registers: their results
+    # feed vector arithmetic at once, and the accumulation-register form adds one copy
+    # per result register
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-result",
 ]
 

@@ -27,10 +27,20 @@
 // line) into one of two tile buffers, while they compute the other. Wave v computes
 // super-blocks 5v .. 5v + 4 of all 16 rows; the four partial sums of a row meet in
 // LDS and wave t adds them for token t and stores y. Its activation operands (A, C
-// and the q8 block scales) depend only on the wave's K quarter, so they are loaded
-// once and stay in registers for every tile. Per tile: two barriers (buffer free;
-// tile landed), each wave's own copies awaited with a counted wait (vm_wait), as
-// the compiler does not count buffer-to-LDS loads.
+// and the q8 block scales, as fp16 pairs) depend only on the wave's K quarter, so they
+// are loaded once and stay in registers for every tile (251 registers at 4 tokens; C
+// read from an LDS table per step instead measured about 4 us slower). Per tile: two
+// barriers (buffer free; tile landed), each wave's own copies awaited with a counted
+// wait (vm_wait), as the compiler does not count buffer-to-LDS loads.
+//
+// What bounds it: two 66 KB tile buffers are what LDS holds, so a CU has at most one
+// tile in flight, and none between the landing of one tile's copies and the issue of
+// the next, which waits for the compute of the tile before. The copies alone (no
+// arithmetic) run the matrix in 92 us, the arithmetic alone in 58 us. Measured and not
+// kept: eight waves (two per K quarter, each two of a super-block's four steps) and
+// codes built with 64-bit shifts were slower at 3 tokens and equal at 4; a last round
+// of small tiles spread over every workgroup (instead of 32 of 256 workgroups taking a
+// 38th tile) was slower.
 //
 // Super-block sb of a row, lane K-group g = 2c + a (c the 128-element half, a the
 // 32-element unit inside it): the lane's 32 low-bit bytes (ql 128 sb + 32 g) hold
@@ -51,20 +61,20 @@ namespace {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int TILE_WG = 256;     // four waves
-constexpr int TILE_WAVES = 4;
 constexpr uint32_t TILE_ROWS = 16;
 constexpr uint32_t TILE_NBE = 20;        // super-blocks per row (K = 5120)
 
 template <uint32_t NBE>
 struct TileGeom {
+    static constexpr int WAVES = 4;                             // one per K quarter
     static constexpr uint32_t STRIDE = (uint32_t)kq_row_stride(KQT_Q6_K, NBE);
     static constexpr uint32_t BYTES = TILE_ROWS * STRIDE;
-    static constexpr uint32_t RUNS = (BYTES + 4095u) / 4096u;   // 1 KB copies per wave per tile
-    static constexpr uint32_t BUF = TILE_WAVES * RUNS * 1024u;  // one tile buffer (copies past
-                                                                // the tile land zeros here)
-    static constexpr uint32_t SPW = NBE / TILE_WAVES;           // super-blocks per wave
-    static_assert(NBE % TILE_WAVES == 0, "whole K quarters");
+    static constexpr uint32_t RUNS = (BYTES + 1024u * WAVES - 1u) / (1024u * WAVES);   // 1 KB
+                                                                 // copies per wave per tile
+    static constexpr uint32_t BUF = WAVES * RUNS * 1024u;       // one tile buffer (copies past
+                                                                 // the tile land zeros here)
+    static constexpr uint32_t SPW = NBE / 4;                    // super-blocks per K quarter
+    static_assert(NBE % 4 == 0, "whole K quarters");
     static_assert(RUNS <= 63, "vmcnt range");
 };
 
@@ -84,46 +94,66 @@ __device__ __forceinline__ i32x4 as_i32x4(uint4 v)
 }
 
 template <int NT, uint32_t NBE>
-__global__ __launch_bounds__(TILE_WG) void mmvq_tiles(const uint8_t *__restrict__ w,
+__global__ __launch_bounds__(256) void mmvq_tiles(const uint8_t *__restrict__ w,
                                                       const int8_t *__restrict__ qs,
                                                       const uint16_t *__restrict__ d8,
                                                       float *__restrict__ y, uint32_t N,
                                                       uint32_t ldy)
 {
-    using G = TileGeom<NBE>;
-    constexpr uint32_t SPW = G::SPW;
+    using TG = TileGeom<NBE>;
+    constexpr int WAVES = TG::WAVES;
+    constexpr uint32_t SPW = TG::SPW;
     constexpr uint32_t K = 256u * NBE;
-    __shared__ __align__(16) uint8_t tbuf[2 * G::BUF];
-    __shared__ float part[2][TILE_WAVES][4][TILE_ROWS];
+    __shared__ __align__(16) uint8_t tbuf[2 * TG::BUF];
+    __shared__ float part[2][WAVES][4][TILE_ROWS];
 
     const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // K quarter
     const uint32_t r = lane & 15u, g = lane >> 4, c = g >> 1, a = g & 1u;
     const uint32_t T = (N + TILE_ROWS - 1u) / TILE_ROWS;
     if (blockIdx.x >= T)
         return;
     const uint32_t S = (T - 1u - blockIdx.x) / gridDim.x + 1u;   // this workgroup's tiles
+    // first row and rows of tile s of this workgroup, tile blockIdx.x + s * gridDim.x
+    // (none past the last)
+    auto tile_rows = [&](uint32_t s, uint32_t &r0) -> uint32_t {
+        r0 = (blockIdx.x + s * gridDim.x) * TILE_ROWS;
+        return r0 < N ? (N - r0 < TILE_ROWS ? N - r0 : TILE_ROWS) : 0u;
+    };
     const uint32_t lds0 = lds_offset(tbuf);
 
-    // tile s of this workgroup (blockIdx.x + s * gridDim.x) into buffer b: rows below
-    // N only (the copies of rows past N, and of a tile past the last, write zeros
-    // without a memory request)
+    // tile s into buffer b (the copies of rows past the tile's, and of a tile past the
+    // last, write zeros without a memory request)
     auto copy_tile = [&](uint32_t b, uint32_t s) {
-        const uint32_t r0 = (blockIdx.x + s * gridDim.x) * TILE_ROWS;
-        const uint32_t rows = r0 < N ? (N - r0 < TILE_ROWS ? N - r0 : TILE_ROWS) : 0u;
+        uint32_t r0;
+        const uint32_t rows = tile_rows(s, r0);
         const __amdgpu_buffer_rsrc_t rs =
-            buf_desc(w + (size_t)(rows ? r0 : 0u) * G::STRIDE, rows * G::STRIDE);
+            buf_desc(w + (size_t)(rows ? r0 : 0u) * TG::STRIDE, rows * TG::STRIDE);
 #pragma unroll
-        for (uint32_t m = 0; m < G::RUNS; ++m) {
-            const uint32_t run = v + TILE_WAVES * m;
-            dma_b128(rs, 16u * lane, 1024u * run, lds0 + b * G::BUF + 1024u * run);
+        for (uint32_t m = 0; m < TG::RUNS; ++m) {
+            const uint32_t run = wv + WAVES * m;
+            dma_b128(rs, 16u * lane, 1024u * run, lds0 + b * TG::BUF + 1024u * run);
         }
     };
     copy_tile(0, 0);
+    // wave t (a token) stores tile s's outputs for token t: the waves' partial sums of
+    // row `lane`, added in wave order
+    auto store_tile = [&](uint32_t s, const float (&pp)[WAVES][4][TILE_ROWS]) {
+        uint32_t r0;
+        const uint32_t rows = tile_rows(s, r0);
+        if (lane < rows) {
+            float tot = pp[0][wv][lane];
+#pragma unroll
+            for (int u = 1; u < WAVES; ++u)
+                tot += pp[u][wv][lane];
+            y[(size_t)wv * ldy + r0 + lane] = tot;
+        }
+    };
 
-    // the wave's activation operands, the same for every tile
+    // the wave's activation operands, the same for every tile: A and C in registers, the
+    // q8 block scales as fp16 pairs (tokens 0, 1 and 2, 3)
     i32x4 A[4 * SPW], C[4 * SPW];
-    float F[2 * SPW][NT];
+    uint32_t Fh[2 * SPW][2];
     {
         const uint32_t ia = lane & 15u, ta = ia & 3u, sa = ia >> 2;
         const bool live = sa == g && ta < (uint32_t)NT;
@@ -131,7 +161,7 @@ __global__ __launch_bounds__(TILE_WG) void mmvq_tiles(const uint8_t *__restrict_
         const uint32_t xbase = live ? ta * K : NT * K;   // past the extent: zeros
 #pragma unroll
         for (uint32_t m = 0; m < SPW; ++m) {
-            const uint32_t sb = SPW * v + m;
+            const uint32_t sb = SPW * wv + m;
 #pragma unroll
             for (uint32_t j = 0; j < 4; ++j) {
                 const uint32_t off = 256u * sb + 128u * c + 32u * a + 64u * (j >> 1) + 16u * (j & 1u);
@@ -147,9 +177,12 @@ __global__ __launch_bounds__(TILE_WG) void mmvq_tiles(const uint8_t *__restrict_
 #pragma unroll
             for (uint32_t p = 0; p < 2; ++p) {
                 const uint32_t blk = 8u * sb + 4u * c + a + 2u * p;
+                uint32_t hv[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
-                    F[2 * m + p][t] = f16_bits_to_f32(d8[(size_t)t * (K / 32u) + blk]);
+                    hv[t] = d8[(size_t)t * (K / 32u) + blk];
+                Fh[2 * m + p][0] = hv[0] | (hv[1] << 16);
+                Fh[2 * m + p][1] = hv[2] | (hv[3] << 16);
             }
         }
     }
@@ -160,30 +193,25 @@ __global__ __launch_bounds__(TILE_WG) void mmvq_tiles(const uint8_t *__restrict_
         const uint32_t b = s & 1u;
         __syncthreads();            // every wave is done with buffer b ^ 1 (tile s - 1)
         copy_tile(b ^ 1u, s + 1u);
-        vm_wait<(int)G::RUNS>();    // this wave's copies of tile s have landed
+        vm_wait<(int)TG::RUNS>();   // this wave's copies of tile s have landed
         __syncthreads();            // and every wave's
-        if (s > 0 && v < (uint32_t)NT && lane < TILE_ROWS) {
-            // tile s - 1: the four waves' partial sums of row `lane` for token v
-            const float(&pp)[TILE_WAVES][4][TILE_ROWS] = part[b ^ 1u];
-            const float tot = ((pp[0][v][lane] + pp[1][v][lane]) + pp[2][v][lane]) + pp[3][v][lane];
-            const uint32_t row = (blockIdx.x + (s - 1u) * gridDim.x) * TILE_ROWS + lane;
-            if (row < N)
-                y[(size_t)v * ldy + row] = tot;
-        }
-        const uint8_t *rb = tbuf + b * G::BUF + r * G::STRIDE;
+        if (s > 0 && wv < (uint32_t)NT)
+            store_tile(s - 1u, part[b ^ 1u]);
+        const uint8_t *rb = tbuf + b * TG::BUF + r * TG::STRIDE;
         float acc[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t)
             acc[t] = 0.0f;
 #pragma unroll
         for (uint32_t m = 0; m < SPW; ++m) {
-            const uint32_t sb = SPW * v + m;
+            const uint32_t sb = SPW * wv + m;
             const uint4 q0 = *reinterpret_cast<const uint4 *>(rb + 128u * sb + 32u * g);
             const uint4 q1 = *reinterpret_cast<const uint4 *>(rb + 128u * sb + 32u * g + 16u);
             const uint4 h0 = *reinterpret_cast<const uint4 *>(rb + 128u * NBE + 64u * sb + 32u * c);
             const uint4 h1 = *reinterpret_cast<const uint4 *>(rb + 128u * NBE + 64u * sb + 32u * c + 16u);
-            const uint2 sc = *reinterpret_cast<const uint2 *>(rb + 192u * NBE + 16u * sb + 8u * c);
             const uint32_t dbits = *reinterpret_cast<const uint16_t *>(rb + 208u * NBE + 2u * sb);
+            const float d = f16_bits_to_f32(dbits);
+            const uint2 sc = *reinterpret_cast<const uint2 *>(rb + 192u * NBE + 16u * sb + 8u * c);
             uint4 k0, k1, k2, k3;
             uint32_t hm;
             hm = h0.x & M; k0.x = codes_lo(q0.x, hm, up); k2.x = codes_hi(q0.x, hm, sh);
@@ -202,13 +230,15 @@ __global__ __launch_bounds__(TILE_WG) void mmvq_tiles(const uint8_t *__restrict_
             const int s1 = (int)(int8_t)(uint8_t)(sc.x >> (16u * a + 8u));
             const int s2 = (int)(int8_t)(uint8_t)(sc.y >> (16u * a));
             const int s3 = (int)(int8_t)(uint8_t)(sc.y >> (16u * a + 8u));
-            const float d = f16_bits_to_f32(dbits);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const int i0 = __mul24(s0, D0[t]) + __mul24(s1, D1[t]);
                 const int i1 = __mul24(s2, D2[t]) + __mul24(s3, D3[t]);
-                acc[t] = __builtin_fmaf(d, (float)i0 * F[2 * m][t], acc[t]);
-                acc[t] = __builtin_fmaf(d, (float)i1 * F[2 * m + 1][t], acc[t]);
+                const float f0 = f16_bits_to_f32(Fh[2 * m][t >> 1] >> (16 * (t & 1)));
+                const float f1 = f16_bits_to_f32(Fh[2 * m + 1][t >> 1] >> (16 * (t & 1)));
+                // d * (d8 * i0 + d8' * i1): the super-block's two q8 blocks, then its scale
+                const float u = __builtin_fmaf(f1, (float)i1, (float)i0 * f0);
+                acc[t] = __builtin_fmaf(d, u, acc[t]);
             }
         }
         // row r's sum over the four K-groups (the same value in all four lanes), then
@@ -221,16 +251,11 @@ __global__ __launch_bounds__(TILE_WG) void mmvq_tiles(const uint8_t *__restrict_
             x += __shfl_xor(x, 16);
             mine = g == (uint32_t)t ? x : mine;
         }
-        part[b][v][g][r] = mine;
+        part[b][wv][g][r] = mine;
     }
     __syncthreads();
-    if (v < (uint32_t)NT && lane < TILE_ROWS) {
-        const float(&pp)[TILE_WAVES][4][TILE_ROWS] = part[(S - 1u) & 1u];
-        const float tot = ((pp[0][v][lane] + pp[1][v][lane]) + pp[2][v][lane]) + pp[3][v][lane];
-        const uint32_t row = (blockIdx.x + (S - 1u) * gridDim.x) * TILE_ROWS + lane;
-        if (row < N)
-            y[(size_t)v * ldy + row] = tot;
-    }
+    if (wv < (uint32_t)NT)
+        store_tile(S - 1u, part[(S - 1u) & 1u]);
     // no copy may still be landing in LDS when the workgroup ends
     vm_wait<0>();
 }
@@ -239,23 +264,25 @@ template <int NT>
 hipError_t launch_nt(const uint8_t *w, const int8_t *qs, const uint16_t *d8, float *y,
                      uint32_t N, uint32_t ldy, int num_cu, hipStream_t s)
 {
+    constexpr int threads = 64 * TileGeom<TILE_NBE>::WAVES;
     const void *kern = (const void *)mmvq_tiles<NT, TILE_NBE>;
     int fit = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&fit, kern, TILE_WG, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&fit, kern, threads, 0) != hipSuccess ||
         fit < 1)
         return hipErrorInvalidValue;
     const uint32_t T = (N + TILE_ROWS - 1u) / TILE_ROWS;
     const uint32_t full = (uint32_t)num_cu * (uint32_t)fit;
     const uint32_t grid = T < full ? T : full;
     void *args[] = {(void *)&w, (void *)&qs, (void *)&d8, (void *)&y, (void *)&N, (void *)&ldy};
-    return hipLaunchKernel(kern, dim3(grid), dim3(TILE_WG), args, 0, s);
+    return hipLaunchKernel(kern, dim3(grid), dim3(threads), args, 0, s);
 }
 
 }  // namespace
 
 // Measured against the register row pairs (graph-replayed GEMV, lm_head 152064 x 5120,
-// one MI355X): 4 tokens 101.4 -> 97.9 us, 3 tokens 95.9 -> 95.1; at 2 tokens, where
-// the row pairs' arithmetic is light, 92.6 -> 94.8, so 2 tokens keep the row pairs.
+// one MI355X, both libraries on one box): 4 tokens 100.5-102.2 -> 95.9-97.9 us, 3 tokens
+// 95.4-96.0 -> 94.3-95.0; at 2 tokens, where the row pairs' arithmetic is light, the
+// first form of this kernel measured 92.6 -> 94.8, so 2 tokens keep the row pairs.
 bool tiles_ok(int type, int64_t N, int64_t K, int nt)
 {
     return type == KQT_Q6_K && K == 256 * (int64_t)TILE_NBE && nt >= 3 && nt <= 4 &&
