@@ -1016,6 +1016,37 @@ __global__ __launch_bounds__(WG) void mmvq_subdots_kernel(const uint8_t *__restr
     }
 }
 
+// Workgroups of `kern` that fit on one CU at once (its registers and LDS), from the
+// runtime's occupancy calculator. Some long-row kernels need more than the 256
+// registers per lane that two workgroups per CU leave; a grid sized for two would
+// then run in two rounds.
+// lds: the launch's dynamic LDS bytes (the kernel's own static LDS is known to the
+// runtime); past 64 KB the kernel is first allowed that much.
+// Process-wide state: the answer is kept per (current device, kernel, lds) for the
+// life of the process, behind a mutex, so the query runs once per kernel and size.
+int wg_fit(const void *kern, uint32_t lds)
+{
+    static std::mutex mu;
+    static std::map<std::tuple<int, const void *, uint32_t>, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    const auto key = std::make_tuple(dev, kern, lds);
+    auto it = cache.find(key);
+    if (it != cache.end())
+        return it->second;
+    if (lds > 65536u &&
+        hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
+            hipSuccess)
+        return 0;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, WG, lds) != hipSuccess || n < 1)
+        return 0;
+    cache.emplace(key, n);
+    return n;
+}
+
 namespace {
 
 // The fixed-length kernel's shape: rows in flight per wave, whether the activation
@@ -1086,37 +1117,6 @@ struct GemvArgs {
     float *y;
     uint32_t N, nbe, stride, K, ldy;
 };
-
-// Workgroups of `kern` that fit on one CU at once (its registers and LDS), from the
-// runtime's occupancy calculator. Some long-row kernels need more than the 256
-// registers per lane that two workgroups per CU leave; a grid sized for two would
-// then run in two rounds.
-// lds: the launch's dynamic LDS bytes (the kernel's own static LDS is known to the
-// runtime); past 64 KB the kernel is first allowed that much.
-// Process-wide state: the answer is kept per (current device, kernel, lds) for the
-// life of the process, behind a mutex, so the query runs once per kernel and size.
-int wg_fit(const void *kern, uint32_t lds = 0)
-{
-    static std::mutex mu;
-    static std::map<std::tuple<int, const void *, uint32_t>, int> cache;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess)
-        return 0;
-    std::lock_guard<std::mutex> lock(mu);
-    const auto key = std::make_tuple(dev, kern, lds);
-    auto it = cache.find(key);
-    if (it != cache.end())
-        return it->second;
-    if (lds > 65536u &&
-        hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
-            hipSuccess)
-        return 0;
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, WG, lds) != hipSuccess || n < 1)
-        return 0;
-    cache.emplace(key, n);
-    return n;
-}
 
 // Workgroups: whole multiples of the CU count (an uneven count leaves some CUs one
 // workgroup short), never more waves than rows, at most as many per CU as fit.

@@ -27,6 +27,10 @@ struct MmvqPlan {
 
 MmvqPlan plan_mmvq(int type, int64_t N, int64_t K, int nt, int num_cu);
 
+// Workgroups of `kern` (256 threads) that fit on one CU at once, with `lds` bytes of
+// dynamic LDS; 0 if the runtime cannot say. Kept per device, kernel and size.
+int wg_fit(const void *kern, uint32_t lds = 0);
+
 // The q6_K GEMV at 3-4 tokens on 16-row tiles with the int8 matrix cores (tiles.hip):
 // rows of 20 super-blocks. qs, d8: the token group's q8 plane fields; y: [nt][ldy].
 bool tiles_ok(int type, int64_t N, int64_t K, int nt);

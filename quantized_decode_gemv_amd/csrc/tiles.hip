@@ -264,11 +264,10 @@ template <int NT>
 hipError_t launch_nt(const uint8_t *w, const int8_t *qs, const uint16_t *d8, float *y,
                      uint32_t N, uint32_t ldy, int num_cu, hipStream_t s)
 {
-    constexpr int threads = 64 * TileGeom<TILE_NBE>::WAVES;
+    constexpr int threads = 64 * TileGeom<TILE_NBE>::WAVES;   // 256, the size wg_fit assumes
     const void *kern = (const void *)mmvq_tiles<NT, TILE_NBE>;
-    int fit = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&fit, kern, threads, 0) != hipSuccess ||
-        fit < 1)
+    const int fit = wg_fit(kern);
+    if (fit < 1)
         return hipErrorInvalidValue;
     const uint32_t T = (N + TILE_ROWS - 1u) / TILE_ROWS;
     const uint32_t full = (uint32_t)num_cu * (uint32_t)fit;
