@@ -267,7 +267,8 @@ int mmvq_kq_q8_subdots(int type, const void *w_dpl, const void *q8, int32_t *dot
  *   3 a fixed-length kernel with two rows per wave (2..4 tokens, K = 1024, 3072 or
  *     5120, whose rows hold an odd multiple of 32 chunks, and at least 4 rows per wave
  *     of its grid); each half of the wave takes one row's last chunk slot;
- *   4 16-row tiles on the int8 matrix cores (q6_K, 3 or 4 tokens, K = 5120, N >= 16):
+ *   4 16-row tiles on the int8 matrix cores (q6_K, K = 5120, 4 tokens with at least 12
+ *     tiles of 16 rows per CU, 3 tokens with at least 24):
  *     a workgroup's four waves copy 16 consecutive rows into LDS and each takes a
  *     quarter of K; each output adds the four quarters in a fixed order;
  * out6[3] = where activation operands live across rows (0: re-read from the q8

@@ -1389,7 +1389,7 @@ hipError_t launch_mmvq_fmt(const uint8_t *w, const uint8_t *q8, float *y, int64_
         a.K = (uint32_t)K;
         a.ldy = (uint32_t)N;
         hipError_t e;
-        if (tiles_ok(F::TYPE, N, K, n)) {
+        if (tiles_ok(F::TYPE, N, K, n, num_cu)) {
             e = launch_tiles(w, a.qs, a.d8, a.y, N, a.ldy, n, num_cu, s);
         } else if (pairs_ok(F::TYPE, n, cpl, N, K, num_cu)) {
             switch (n) {
@@ -1512,7 +1512,7 @@ MmvqPlan plan_mmvq(int type, int64_t N, int64_t K, int nt, int num_cu)
     p.unrolled = p.cpl <= MAX_CPL;
     p.launches = (nt + MAX_NT_KERNEL - 1) / MAX_NT_KERNEL;
     const int nt0 = nt < MAX_NT_KERNEL ? nt : MAX_NT_KERNEL;
-    if (tiles_ok(type, N, K, nt0)) {
+    if (tiles_ok(type, N, K, nt0, num_cu)) {
         p.tiles = true;
         p.act_mode = ACT_REGS;
         p.depth = 2;

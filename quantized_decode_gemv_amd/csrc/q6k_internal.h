@@ -32,8 +32,9 @@ MmvqPlan plan_mmvq(int type, int64_t N, int64_t K, int nt, int num_cu);
 int wg_fit(const void *kern, uint32_t lds = 0);
 
 // The q6_K GEMV at 3-4 tokens on 16-row tiles with the int8 matrix cores (tiles.hip):
-// rows of 20 super-blocks. qs, d8: the token group's q8 plane fields; y: [nt][ldy].
-bool tiles_ok(int type, int64_t N, int64_t K, int nt);
+// rows of 20 super-blocks, at least 12 (4 tokens) or 24 (3 tokens) tiles per CU. qs, d8:
+// the token group's q8 plane fields; y: [nt][ldy].
+bool tiles_ok(int type, int64_t N, int64_t K, int nt, int num_cu);
 hipError_t launch_tiles(const uint8_t *w, const int8_t *qs, const uint16_t *d8, float *y,
                         int64_t N, int64_t ldy, int nt, int num_cu, hipStream_t s);
 // type: a KqType of kq_format.h (the weight rows are that type's split-plane rows).

@@ -278,14 +278,21 @@ hipError_t launch_nt(const uint8_t *w, const int8_t *qs, const uint16_t *d8, flo
 
 }  // namespace
 
-// Measured against the register row pairs (graph-replayed GEMV, lm_head 152064 x 5120,
-// one MI355X, both libraries on one box): 4 tokens 100.5-102.2 -> 95.9-97.9 us, 3 tokens
-// 95.4-96.0 -> 94.3-95.0; at 2 tokens, where the row pairs' arithmetic is light, the
-// first form of this kernel measured 92.6 -> 94.8, so 2 tokens keep the row pairs.
-bool tiles_ok(int type, int64_t N, int64_t K, int nt)
+// Measured against the row pairs (graph-replayed GEMV at K = 5120, one MI355X, both
+// libraries on one box): lm_head 152064 rows at 4 tokens 100.5-102.2 -> 95.9-98.0 us (the
+// pairs through an LDS ring), at 3 tokens 95.4-96.0 -> 94.3-95.0. Each workgroup pays a
+// fixed start (its operands, the first tile's copy) that only many tiles amortize. At 4
+// tokens the tiles beat the register row pairs from 49152 rows (12 tiles per CU: 37.8 ->
+// 37.0 us; 65536 rows 47.6 -> 45.8) and lose below (32768 rows 25.4 -> 26.8, 1024 rows
+// 4.0 -> 7.4); at 3 tokens they win from 98304 rows (24 per CU: 62.8 -> 62.5 us; 131072
+// rows 83.1 -> 81.7). At 2 tokens the first form of this kernel measured 92.6 -> 94.8 us
+// at lm_head, so 2 tokens keep the row pairs.
+bool tiles_ok(int type, int64_t N, int64_t K, int nt, int num_cu)
 {
-    return type == KQT_Q6_K && K == 256 * (int64_t)TILE_NBE && nt >= 3 && nt <= 4 &&
-           N >= (int64_t)TILE_ROWS;
+    if (type != KQT_Q6_K || K != 256 * (int64_t)TILE_NBE || nt < 3 || nt > 4)
+        return false;
+    const int64_t tiles = (N + TILE_ROWS - 1) / TILE_ROWS;
+    return tiles >= (int64_t)(nt == 4 ? 12 : 24) * num_cu;
 }
 
 hipError_t launch_tiles(const uint8_t *w, const int8_t *qs, const uint16_t *d8, float *y,

@@ -200,9 +200,11 @@ def test_plan_pairs_rule(qtype, nbe, nt, N):
     # 32 chunks, at most 3 chunks per lane, and at least two pairs per wave of the
     # grid (one workgroup per CU: 1024 waves on 256 CUs)
     # q6_K rows of 20 super-blocks at 3 or 4 tokens take the matrix-core tiles instead
-    # (16 rows per tile, one workgroup per CU, two tile buffers)
+    # when there are enough tiles of 16 rows (4 tokens: 12 per CU, 3 tokens: 24; one
+    # workgroup per CU, two tile buffers)
     p = q.mmvq_plan(N, 256 * nbe, nt, 256, qtype)
-    tiles = qtype == 14 and nbe == 20 and min(nt, 4) >= 3 and N >= 16
+    tiles = (qtype == 14 and nbe == 20 and min(nt, 4) >= 3
+             and -(-N // 16) >= (12 if min(nt, 4) == 4 else 24) * 256)
     assert p["tiles"] == tiles
     if tiles:
         assert not p["paired"] and p["grid"] == min(-(-N // 16), 256)
@@ -217,12 +219,29 @@ def test_plan_pairs_rule(qtype, nbe, nt, N):
         assert p["depth"] == 2 and p["act_mode"] == 1
 
 
+@pytest.mark.parametrize("num_cu", [256, 80, 304])
+@pytest.mark.parametrize("nt", [2, 3, 4, 5, 8])
+def test_plan_tiles_threshold(num_cu, nt):
+    # the tiles take q6_K K = 5120 from 12 tiles of 16 rows per CU at 4 tokens and 24 at
+    # 3 (per launch of up to 4 tokens); one row fewer keeps the row pairs
+    n = min(nt, 4)
+    if n < 3:
+        assert not q.mmvq_plan(1 << 20, 5120, nt, num_cu)["tiles"]
+        return
+    first = 16 * (12 if n == 4 else 24) * num_cu
+    at, below = q.mmvq_plan(first, 5120, nt, num_cu), q.mmvq_plan(first - 16, 5120, nt, num_cu)
+    assert at["tiles"] and at["grid"] == num_cu and not below["tiles"]
+    assert q.mmvq_plan(first - 15, 5120, nt, num_cu)["tiles"]
+    assert not q.mmvq_plan(first, 5120, nt, num_cu, 12)["tiles"]
+    assert not q.mmvq_plan(first, 4864, nt, num_cu)["tiles"]
+
+
 @pytest.mark.parametrize("N", [1, 2, 3, 63, 64, 65, 1023, 1024, 1025, 4096, 152064])
 @pytest.mark.parametrize("nt", [1, 2, 4])
 def test_plan_grid_is_whole_cus_or_one_wave_per_row(N, nt):
     p = q.mmvq_plan(N, 5120, nt, 256)
-    # 16-row tiles at 4 tokens: one workgroup per tile up to one per CU
-    assert p["tiles"] == (nt == 4 and N >= 16)
+    # 16-row tiles at 4 tokens from 12 tiles per CU: one workgroup per CU
+    assert p["tiles"] == (nt == 4 and -(-N // 16) >= 12 * 256)
     if p["tiles"]:
         assert p["grid"] == min(-(-N // 16), 256)
         return

@@ -126,7 +126,8 @@ def _gemv(qtype, W, qs, d16, N, K, nt):
 # kernel; q6_K matrix-core tiles
 SHAPES = [("rows-cpl1", 64, 1024, 1), ("rows-cpl3", 15, 5120, 3), ("pairs", 4099, 5120, 2),
           ("shared", 2999, 18944, 1), ("shared-nt2", 1500, 13824, 2),
-          ("lds", 8192, 256 * 88, 1), ("long", 67, 256 * 100, 2), ("tiles", 4099, 5120, 4)]
+          ("lds", 8192, 256 * 88, 1), ("long", 67, 256 * 100, 2),
+          ("tiles", 16 * 12 * 256 + 3, 5120, 4)]
 
 
 # (q4_K / q5_K long rows at one token are shared by a workgroup instead of staged; the

@@ -135,15 +135,15 @@ def test_shared_rows_random(N, nbe, nt):
 
 # Two rows per wave (2..4 tokens, rows of an odd multiple of 32 chunks: nbe 4, 12, 20):
 # every chunk count per lane 1..3, an odd N (the last pair has one row), and nt = 5 (a
-# paired launch of 4 tokens, then a one-wave launch of 1). At 3 and 4 tokens rows of 20
-# super-blocks take the matrix-core tiles instead (test_tiles_random).
+# paired launch of 4 tokens, then a one-wave launch of 1). With many more rows, rows of 20
+# super-blocks at 3 and 4 tokens take the matrix-core tiles instead (test_tiles_random).
 @pytest.mark.parametrize("nbe", [4, 12, 20])
 @pytest.mark.parametrize("N,nt", [(4095, 2), (4097, 3), (8192, 4), (4099, 5), (4095, 4),
                                   (4097, 4)])
 def test_pairs_random(nbe, N, nt):
     K = 256 * nbe
     plan = q.mmvq_plan(N, K, nt, 256)
-    assert plan["paired"] == (nbe != 20 or nt == 2) and plan["tiles"] == (nbe == 20 and nt >= 3)
+    assert plan["paired"] and not plan["tiles"]
     raw = q6ksynth.raw_q6k(N, K, seed=N * 3 + nbe + nt)
     dpl = dpl_from_raw(raw, N, K)
     x = np.stack([q6ksynth.activation("outlier", K, 1400 + c) for c in range(nt)])
@@ -153,24 +153,29 @@ def test_pairs_random(nbe, N, nt):
     check_y(y, y_or, A, f"pairs N={N} nbe={nbe} nt={nt}")
 
 
-# 16-row tiles on the int8 matrix cores (q6_K, K = 5120, 3 or 4 tokens per launch):
-# a single tile, a ragged last tile (N % 16 = 1 and 15), fewer tiles than CUs, more
-# tiles than CUs with an uneven count per workgroup (4097 rows: 257 tiles, one
-# workgroup takes two), 5 and 7 tokens (a tile launch of 4, then 1 or 3 more), and
-# a zero activation row next to nonzero ones (its outputs must be exactly 0).
-@pytest.mark.parametrize("N,nt", [(16, 4), (17, 3), (31, 4), (100, 3), (4097, 4), (4111, 3),
-                                  (4096 * 3 + 5, 4), (1000, 5), (999, 7)])
+# 16-row tiles on the int8 matrix cores (q6_K, K = 5120; 4 tokens per launch from 12 tiles
+# per CU, 3 from 24): the first row count that takes them at 4 and at 3 tokens (whole
+# rounds of tiles), a ragged last tile (N % 16 = 1 and 15) with a partial last round, 5
+# and 7 tokens (a tile launch of 4, then 1 or 3 more), and a zero activation row next to
+# nonzero ones (its outputs must be exactly 0).
+TILES_4 = 16 * 12 * 256
+TILES_3 = 16 * 24 * 256
+
+
+@pytest.mark.parametrize("N,nt", [(TILES_4, 4), (TILES_4 + 1, 4), (TILES_3, 3), (TILES_3 + 15, 3),
+                                  (TILES_4 + 4111, 4), (TILES_4 + 333, 5), (TILES_4 + 17, 7)])
 def test_tiles_random(N, nt):
     K = 5120
     plan = q.mmvq_plan(N, K, nt, 256)
     assert plan["tiles"] and plan["grid"] == min(-(-N // 16), 256)
+    say(f"tiles N={N} nt={nt}")
     raw = q6ksynth.raw_q6k(N, K, seed=N * 5 + nt)
     dpl = dpl_from_raw(raw, N, K)
     x = np.stack([q6ksynth.activation("outlier", K, 1600 + c) for c in range(nt)])
     x[1] = 0.0
     qs, d = oracle.quant_q8(x)
     y = run_mmvq(dpl, make_plane(qs, d), N, K, nt)
-    y_or, A = oracle.mmvq(oracle.RAW, raw, N, K, qs, d)
+    y_or, A = oracle.mmvq(oracle.RAW, raw, N, K, qs, d, nthreads=oracle_threads())
     assert np.all(y[1] == 0)
     check_y(y, y_or, A, f"tiles N={N} nt={nt}")
 
