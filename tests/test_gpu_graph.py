@@ -65,16 +65,20 @@ def _fill(producer, b, K, nt, seed):
         b["x"].copy_(torch.from_numpy(x))
 
 
-# the GEMV kinds: one wave per row, row pairs (8192 x 5120 at 4 tokens), rows shared
-# by a workgroup (3584 x 18944, 3000 x 13824 at 4 tokens), the generic stepping kernel
+# the GEMV kinds: one wave per row, row pairs (8192 x 5120 at 4 tokens), the matrix-core
+# tiles (49152 x 5120 at 4 tokens: buffer-to-LDS copies, counted waits and barriers),
+# rows shared by a workgroup (3584 x 18944, 3000 x 13824 at 4 tokens), the generic
+# stepping kernel
 @pytest.mark.parametrize("producer,N,K,nt", [("rmsnorm", 4096, 5120, 1), ("rmsnorm", 2048, 5120, 4),
-                                             ("rmsnorm", 8192, 5120, 4),
+                                             ("rmsnorm", 8192, 5120, 4), ("rmsnorm", 49152, 5120, 4),
                                              ("swiglu", 1024, 13824, 1), ("swiglu", 3584, 18944, 1),
                                              ("quant", 64, 1024, 2), ("quant", 3000, 13824, 4),
                                              ("quant", 333, 256 * 97, 5),
                                              ("fused", 4096, 5120, 1), ("fused", 1024, 5120, 2),
                                              ("formb", 4096, 5120, 1)])
 def test_graph_replays_match_eager(producer, N, K, nt):
+    if N == 49152:
+        assert q.mmvq_plan(N, K, nt, 256)["tiles"]
     raw = q6ksynth.raw_q6k(N, K, seed=N + K)
     W = dpl_from_raw(raw, N, K)
     b = _buffers(producer, K, nt)
