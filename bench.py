@@ -76,9 +76,17 @@ def log(*a):
 
 
 def _code_only(text: str) -> str:
-    """The source without its comments, trailing blanks and empty lines, so that an
-    edit of comments alone keeps the hash (the kernels are the same)."""
-    out, i, n = [], 0, len(text)
+    """The source without its comments, every run of blanks and line breaks outside
+    string literals made one space, so that an edit of comments or layout alone keeps
+    the hash (the kernels are the same)."""
+    parts, buf, i, n = [], [], 0, len(text)
+
+    def flush():
+        code = " ".join("".join(buf).split())
+        if code:
+            parts.append(code)
+        buf.clear()
+
     while i < n:
         if text.startswith("//", i):
             j = text.find("\n", i)
@@ -86,17 +94,19 @@ def _code_only(text: str) -> str:
         elif text.startswith("/*", i):
             j = text.find("*/", i + 2)
             i = n if j < 0 else j + 2
+            buf.append(" ")
         elif text[i] in "\"'":
             q, j = text[i], i + 1
             while j < n and text[j] != q:
                 j += 2 if text[j] == "\\" else 1
-            out.append(text[i:j + 1])
+            flush()
+            parts.append(text[i:j + 1])
             i = j + 1
         else:
-            out.append(text[i])
+            buf.append(text[i])
             i += 1
-    lines = ("".join(out)).split("\n")
-    return "\n".join(l.rstrip() for l in lines if l.strip())
+    flush()
+    return " ".join(parts)
 
 
 def kernel_hash() -> str:

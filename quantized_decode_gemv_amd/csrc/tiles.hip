@@ -51,7 +51,8 @@
 // 8c + 2a + {0, 1, 4, 5}, whose scales are bytes 2a + {0, 1, 4, 5} of the 8-byte group
 // at 16 sb + 8c of the scale plane. Steps 0 and 1 lie in one q8 block (8 sb + 4c + a),
 // steps 2 and 3 in block + 2, so each pair's two scaled dots add exactly in int32
-// (|sc * D| < 2^23) before one conversion.
+// (|sc * D| <= 128 * 16 * 32 * 128 = 2^23, their sum at most 2^24, exact in f32) before
+// one conversion.
 
 #include "q6k_internal.h"
 #include "q6k_unit.h"
@@ -95,10 +96,9 @@ __device__ __forceinline__ i32x4 as_i32x4(uint4 v)
 
 template <int NT, uint32_t NBE>
 __global__ __launch_bounds__(256) void mmvq_tiles(const uint8_t *__restrict__ w,
-                                                      const int8_t *__restrict__ qs,
-                                                      const uint16_t *__restrict__ d8,
-                                                      float *__restrict__ y, uint32_t N,
-                                                      uint32_t ldy)
+                                                  const int8_t *__restrict__ qs,
+                                                  const uint16_t *__restrict__ d8,
+                                                  float *__restrict__ y, uint32_t N, uint32_t ldy)
 {
     using TG = TileGeom<NBE>;
     constexpr int WAVES = TG::WAVES;
