@@ -36,11 +36,15 @@
 // What bounds it: two 66 KB tile buffers are what LDS holds, so a CU has at most one
 // tile in flight, and none between the landing of one tile's copies and the issue of
 // the next, which waits for the compute of the tile before. The copies alone (no
-// arithmetic) run the matrix in 92 us, the arithmetic alone in 58 us. Measured and not
-// kept: eight waves (two per K quarter, each two of a super-block's four steps) and
-// codes built with 64-bit shifts were slower at 3 tokens and equal at 4; a last round
-// of small tiles spread over every workgroup (instead of 32 of 256 workgroups taking a
-// 38th tile) was slower.
+// arithmetic) run the matrix in 92 us, the arithmetic alone in 58 us. Rows past the
+// last whole round of 16-row tiles are shared out evenly, one short tile per workgroup
+// (at lm_head 2 rows each, where 32 of 256 workgroups would otherwise take a 38th tile
+// alone); with whole tiles known to be 16 rows the loop also compiles tighter (1.3 us
+// less at 65536 rows, which have no remainder). Measured and not kept: eight waves (two
+// per K quarter, each two of a super-block's four steps) and codes built with 64-bit
+// shifts were slower at 3 tokens and equal at 4; loading the activation operands into
+// the first tile's buffer, or into an LDS area of their own beside two smaller tiles,
+// was slower at 4 tokens.
 //
 // Super-block sb of a row, lane K-group g = 2c + a (c the 128-element half, a the
 // 32-element unit inside it): the lane's 32 low-bit bytes (ql 128 sb + 32 g) hold
@@ -110,15 +114,24 @@ __global__ __launch_bounds__(256) void mmvq_tiles(const uint8_t *__restrict__ w,
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // K quarter
     const uint32_t r = lane & 15u, g = lane >> 4, c = g >> 1, a = g & 1u;
-    const uint32_t T = (N + TILE_ROWS - 1u) / TILE_ROWS;
-    if (blockIdx.x >= T)
-        return;
-    const uint32_t S = (T - 1u - blockIdx.x) / gridDim.x + 1u;   // this workgroup's tiles
-    // first row and rows of tile s of this workgroup, tile blockIdx.x + s * gridDim.x
-    // (none past the last)
+    // Tiles: FR rounds of whole 16-row tiles, tile blockIdx.x + s * NG in round s (the grid
+    // streams neighbouring tiles together), then, if rows remain (fewer than 16 * NG), one
+    // round in which every workgroup takes an equal share of them (at most 16 rows), so
+    // that no few workgroups run a round alone. Every workgroup has S tiles.
+    const uint32_t NG = gridDim.x;
+    const uint32_t FR = N / (TILE_ROWS * NG);
+    const uint32_t rows_full = FR * TILE_ROWS * NG;
+    const uint32_t rest = N - rows_full;
+    const uint32_t share = (rest + NG - 1u) / NG;
+    const uint32_t S = FR + (rest ? 1u : 0u);
+    // first row and rows of tile s (none past the last)
     auto tile_rows = [&](uint32_t s, uint32_t &r0) -> uint32_t {
-        r0 = (blockIdx.x + s * gridDim.x) * TILE_ROWS;
-        return r0 < N ? (N - r0 < TILE_ROWS ? N - r0 : TILE_ROWS) : 0u;
+        if (s < FR) {
+            r0 = (blockIdx.x + s * NG) * TILE_ROWS;
+            return TILE_ROWS;
+        }
+        r0 = rows_full + blockIdx.x * share;
+        return s == FR && r0 < N ? (N - r0 < share ? N - r0 : share) : 0u;
     };
     const uint32_t lds0 = lds_offset(tbuf);
 
@@ -135,7 +148,6 @@ __global__ __launch_bounds__(256) void mmvq_tiles(const uint8_t *__restrict__ w,
             dma_b128(rs, 16u * lane, 1024u * run, lds0 + b * TG::BUF + 1024u * run);
         }
     };
-    copy_tile(0, 0);
     // wave t (a token) stores tile s's outputs for token t: the waves' partial sums of
     // row `lane`, added in wave order
     auto store_tile = [&](uint32_t s, const float (&pp)[WAVES][4][TILE_ROWS]) {
@@ -151,7 +163,9 @@ __global__ __launch_bounds__(256) void mmvq_tiles(const uint8_t *__restrict__ w,
     };
 
     // the wave's activation operands, the same for every tile: A and C in registers, the
-    // q8 block scales as fp16 pairs (tokens 0, 1 and 2, 3)
+    // q8 block scales as fp16 pairs (tokens 0, 1 and 2, 3). They are requested before the
+    // first tile's copies, as a wave's loads complete in issue order and would otherwise
+    // wait behind them. The scales come as one 16-byte load per token and super-block.
     i32x4 A[4 * SPW], C[4 * SPW];
     uint32_t Fh[2 * SPW][2];
     {
@@ -174,18 +188,26 @@ __global__ __launch_bounds__(256) void mmvq_tiles(const uint8_t *__restrict__ w,
                 for (int t = 0; t < 4; ++t)
                     C[4 * m + j][t] = __builtin_amdgcn_ds_bpermute((int)(4u * (20u * g + t)), ns);
             }
+            // the super-block's 8 q8 block scales of each token (16 bytes), of which
+            // blocks 4c + a and 4c + a + 2 are this lane's
+            const __amdgpu_buffer_rsrc_t dr = buf_desc(d8, NT * (K / 32u) * 2u);
+            uint32_t hv[2][4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const uint4 q = load_b128<POLICY_DEFAULT>(dr, (uint32_t)t * (K / 16u) + 16u * sb);
+                // block 4c + a is half a of word 2c, block 4c + a + 2 half a of word 2c + 1
+                const uint32_t lo = c ? q.z : q.x, hi2 = c ? q.w : q.y;
+                hv[0][t] = (lo >> (16u * a)) & 0xFFFFu;
+                hv[1][t] = (hi2 >> (16u * a)) & 0xFFFFu;
+            }
 #pragma unroll
             for (uint32_t p = 0; p < 2; ++p) {
-                const uint32_t blk = 8u * sb + 4u * c + a + 2u * p;
-                uint32_t hv[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    hv[t] = d8[(size_t)t * (K / 32u) + blk];
-                Fh[2 * m + p][0] = hv[0] | (hv[1] << 16);
-                Fh[2 * m + p][1] = hv[2] | (hv[3] << 16);
+                Fh[2 * m + p][0] = hv[p][0] | (hv[p][1] << 16);
+                Fh[2 * m + p][1] = hv[p][2] | (hv[p][3] << 16);
             }
         }
     }
+    copy_tile(0, 0);
 
     const uint32_t sh = 2u * a, up = 4u - sh;
     const uint32_t M = 0x33333333u << sh;
@@ -278,15 +300,17 @@ hipError_t launch_nt(const uint8_t *w, const int8_t *qs, const uint16_t *d8, flo
 
 }  // namespace
 
-// Measured against the row pairs (graph-replayed GEMV at K = 5120, one MI355X, both
-// libraries on one box): lm_head 152064 rows at 4 tokens 100.5-102.2 -> 95.9-98.0 us (the
-// pairs through an LDS ring), at 3 tokens 95.4-96.0 -> 94.3-95.0. Each workgroup pays a
-// fixed start (its operands, the first tile's copy) that only many tiles amortize. At 4
-// tokens the tiles beat the register row pairs from 49152 rows (12 tiles per CU: 37.8 ->
-// 37.0 us; 65536 rows 47.6 -> 45.8) and lose below (32768 rows 25.4 -> 26.8, 1024 rows
-// 4.0 -> 7.4); at 3 tokens they win from 98304 rows (24 per CU: 62.8 -> 62.5 us; 131072
-// rows 83.1 -> 81.7). At 2 tokens the first form of this kernel measured 92.6 -> 94.8 us
-// at lm_head, so 2 tokens keep the row pairs.
+// Measured against the row pairs (graph-replayed GEMV at K = 5120, one MI355X, the
+// libraries on one box): lm_head 152064 rows at 4 tokens 105.6 -> 95.8 us (the LDS ring
+// this kernel replaced measured 100.5-102.2), at 3 tokens 95.6 -> 94.3. Each
+// workgroup pays a fixed start (its operands, the first tile's copy) that only many
+// tiles amortize. At 4 tokens the tiles beat the register row pairs from 45056 rows (11
+// tiles per CU: 32.9 -> 32.7 us; 49152 rows, 12 per CU, 35.9 -> 35.0) and lose below
+// (40960 rows 30.0 -> 30.3, 32768 rows 24.6 -> 25.7, 1024 rows 4.0 -> 7.4); at 3 tokens
+// from 90112 rows (22 per CU: 58.0 -> 57.3 us; 98304 rows 62.3 -> 62.0; 131072 rows
+// 83.2 -> 80.8) and lose at 81920 (52.5 -> 53.0). The thresholds keep one (4 tokens)
+// and two (3 tokens) tiles per CU of margin above the crossings. At 2 tokens the first
+// form of this kernel measured 92.6 -> 94.8 us at lm_head, so 2 tokens keep the pairs.
 bool tiles_ok(int type, int64_t N, int64_t K, int nt, int num_cu)
 {
     if (type != KQT_Q6_K || K != 256 * (int64_t)TILE_NBE || nt < 3 || nt > 4)
