@@ -49,19 +49,35 @@ struct KqOffs {
     uint32_t qs, qh, sc, dm;
 };
 
-__device__ __forceinline__ KqAct kq_load_act(const int8_t *__restrict__ qs_t,
-                                             const uint16_t *__restrict__ d8_t, uint32_t Q)
+__device__ __forceinline__ ActRaw kq_load_act_raw(const int8_t *__restrict__ qs_t,
+                                                  const uint16_t *__restrict__ d8_t, uint32_t Q)
 {
     const uint32_t k = 64u * (Q >> 1) + 16u * (Q & 1u);
     const uint32_t blk = 2u * (Q >> 1);
+    ActRaw r;
+    r.xa = *reinterpret_cast<const uint4 *>(qs_t + k);
+    r.xb = *reinterpret_cast<const uint4 *>(qs_t + k + 32);
+    r.ha = d8_t[blk];
+    r.hb = d8_t[blk + 1];
+    return r;
+}
+
+__device__ __forceinline__ KqAct kq_act_from_raw(const ActRaw &r)
+{
     KqAct a;
-    a.xa = *reinterpret_cast<const uint4 *>(qs_t + k);
-    a.xb = *reinterpret_cast<const uint4 *>(qs_t + k + 32);
-    a.da = f16_bits_to_f32(d8_t[blk]);
-    a.db = f16_bits_to_f32(d8_t[blk + 1]);
+    a.xa = r.xa;
+    a.xb = r.xb;
+    a.da = f16_bits_to_f32(r.ha);
+    a.db = f16_bits_to_f32(r.hb);
     a.dsa = a.da * (float)sum16_i8(a.xa);
     a.dsb = a.db * (float)sum16_i8(a.xb);
     return a;
+}
+
+__device__ __forceinline__ KqAct kq_load_act(const int8_t *__restrict__ qs_t,
+                                             const uint16_t *__restrict__ d8_t, uint32_t Q)
+{
+    return kq_act_from_raw(kq_load_act_raw(qs_t, d8_t, Q));
 }
 
 // 6-bit scales and mins of the chunk's sub-blocks s = 2j and 2j + 1 (j = (Q >> 1) & 3)
@@ -196,6 +212,13 @@ struct FmtKq {
     {
         return kq_load_act(qs_t, d8_t, Q);
     }
+
+    // act() in two steps: the loads, then the arithmetic on what they returned
+    __device__ static ActRaw act_raw(const int8_t *qs_t, const uint16_t *d8_t, uint32_t Q)
+    {
+        return kq_load_act_raw(qs_t, d8_t, Q);
+    }
+    __device__ static Act act_finish(const ActRaw &r) { return kq_act_from_raw(r); }
 
     // live = false drops the chunk (d = dmin = 0); callers whose operands were
     // dropped already pass true

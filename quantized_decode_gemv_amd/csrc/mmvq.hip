@@ -212,6 +212,38 @@ __device__ __forceinline__ void lane_acts(LaneState<F, NT, CPL, ACT_REGS> &st, c
     }
 }
 
+// lane_acts with a step between the operand loads and their arithmetic: the loads are
+// issued, then `between` (which may issue loads of its own), then the arithmetic,
+// whose waits cover the operand loads only (nothing later is scheduled before it).
+// The same operands as lane_acts.
+template <class F, int NT, int CPL, typename Between>
+__device__ __forceinline__ void lane_acts_around(LaneState<F, NT, CPL, ACT_REGS> &st,
+                                                 const int8_t *qs, const uint16_t *d8,
+                                                 uint32_t K, Between &&between)
+{
+    ActRaw raw[CPL][NT];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            raw[i][t] = F::act_raw(qs + (size_t)t * K, d8 + (size_t)t * (K / 32), st.Q[i]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    between();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            st.act[i][t] = F::act_finish(raw[i][t]);
+            if (!st.live[i])
+                F::drop(st.act[i][t]);
+        }
+    }
+    // the arithmetic stays here, where it waits for the operands only
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 template <class F, int NT, int CPL, int AM>
 __device__ __forceinline__ void load_row(typename F::W (&dst)[CPL], const uint8_t *w,
                                          uint32_t row, uint32_t N, uint32_t stride,
@@ -482,11 +514,26 @@ __global__ __launch_bounds__(WG) void mmvq_rows(const uint8_t *__restrict__ w,
         // compiler's wait counts at the row loop's head then cover the look-ahead rows
         // as well (measured slower on every shape it changed)
         lane_chunks(st, lane, nbe);
-        if constexpr (AM == ACT_REGS)
-            lane_acts(st, qs, d8, K);
         if (wave >= N)
             return;
-        prime_rows<F, NT, CPL, 0, DEPTH - 1, AM>(bufs, w, wave, nw, N, stride, st);
+        // the first rows are requested right behind the operand loads and before
+        // their arithmetic, so the weight stream starts at once: one row with DEPTH 1
+        // (which then walks primed), DEPTH - 1 otherwise. With requests after the
+        // operand arithmetic, which waits for the operand loads, a wave's stream started
+        // up to about 1 us late (per-wave clock stamps, 5120 x 13824 at one token).
+        auto first_rows = [&] {
+            prime_rows<F, NT, CPL, 0, DEPTH == 1 ? 1 : DEPTH - 1, AM>(bufs, w, wave, nw, N,
+                                                                     stride, st);
+        };
+        if constexpr (AM == ACT_REGS)
+            lane_acts_around(st, qs, d8, K, first_rows);
+        else
+            first_rows();
+        if constexpr (DEPTH == 1) {
+            stream_rows_primed<F, NT, CPL, 1, AM>(bufs, w, wave, nw, N, stride, st, qs, d8, K,
+                                                  y, ldy, lane);
+            return;
+        }
     }
     stream_rows<F, NT, CPL, DEPTH, AM>(bufs, w, wave, nw, N, stride, st, qs, d8, K, y, ldy,
                                        lane);
@@ -525,8 +572,10 @@ __global__ __launch_bounds__(WG) void mmvq_split(const uint8_t *__restrict__ w,
     LaneState<F, NT, CPL, AM> st;
     RowBufs<F, CPL> bufs;
     lane_chunks<F, NT, CPL, AM, 256u>(st, threadIdx.x, nbe);
-    lane_acts(st, qs, d8, K);
-    prime_rows<F, NT, CPL, 0, DEPTH - 1, AM>(bufs, wb, 0u, 1u, nr, stride, st);
+    // the first rows right behind the operand loads, before the operand arithmetic
+    lane_acts_around(st, qs, d8, K, [&] {
+        prime_rows<F, NT, CPL, 0, DEPTH - 1, AM>(bufs, wb, 0u, 1u, nr, stride, st);
+    });
     // the shares go where the one-wave kernel stores its outputs: token t of local
     // row j at share[t * R + j]
     stream_rows<F, NT, CPL, DEPTH, AM>(bufs, wb, 0u, 1u, nr, stride, st, qs, d8, K, share, R,

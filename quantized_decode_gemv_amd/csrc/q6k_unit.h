@@ -71,21 +71,44 @@ __device__ __forceinline__ int sdot4_from0(int a, int b)
     return r;
 }
 
+// A chunk's activation bytes as loaded, before any arithmetic on them: the two
+// 16-byte halves and the fp16 bits of their two q8 block scales.
+struct ActRaw {
+    uint4 xa, xb;
+    uint32_t ha, hb;
+};
+
 // qs_t: int8 activations of one token (K entries); d8_t: its fp16 block scales.
-__device__ __forceinline__ ChunkAct load_act(const int8_t *__restrict__ qs_t,
-                                             const uint16_t *__restrict__ d8_t, uint32_t Q)
+__device__ __forceinline__ ActRaw load_act_raw(const int8_t *__restrict__ qs_t,
+                                               const uint16_t *__restrict__ d8_t, uint32_t Q)
 {
     const uint32_t G = Q >> 2;
     const uint32_t k = 16u * (Q + 4u * G);
     const uint32_t blk = 4u * G + ((Q >> 1) & 1u);
+    ActRaw r;
+    r.xa = *reinterpret_cast<const uint4 *>(qs_t + k);
+    r.xb = *reinterpret_cast<const uint4 *>(qs_t + k + 64);
+    r.ha = d8_t[blk];
+    r.hb = d8_t[blk + 2];
+    return r;
+}
+
+__device__ __forceinline__ ChunkAct act_from_raw(const ActRaw &r)
+{
     ChunkAct a;
-    a.xa = *reinterpret_cast<const uint4 *>(qs_t + k);
-    a.xb = *reinterpret_cast<const uint4 *>(qs_t + k + 64);
-    a.da = f16_bits_to_f32(d8_t[blk]);
-    a.db = f16_bits_to_f32(d8_t[blk + 2]);
+    a.xa = r.xa;
+    a.xb = r.xb;
+    a.da = f16_bits_to_f32(r.ha);
+    a.db = f16_bits_to_f32(r.hb);
     a.na = -32 * sum16_i8(a.xa);
     a.nb = -32 * sum16_i8(a.xb);
     return a;
+}
+
+__device__ __forceinline__ ChunkAct load_act(const int8_t *__restrict__ qs_t,
+                                             const uint16_t *__restrict__ d8_t, uint32_t Q)
+{
+    return act_from_raw(load_act_raw(qs_t, d8_t, Q));
 }
 
 // row: start of a dpl row; nbe: super-blocks per row.
@@ -221,6 +244,13 @@ struct FmtQ6K {
     {
         return load_act(qs_t, d8_t, Q);
     }
+
+    // act() in two steps: the loads, then the arithmetic on what they returned
+    __device__ static ActRaw act_raw(const int8_t *qs_t, const uint16_t *d8_t, uint32_t Q)
+    {
+        return load_act_raw(qs_t, d8_t, Q);
+    }
+    __device__ static Act act_finish(const ActRaw &r) { return act_from_raw(r); }
 
     // live = false drops the chunk (d = 0); callers whose operands were dropped
     // already pass true
