@@ -637,8 +637,7 @@ struct PairRing {
 
 template <class F, int NT, int CPL>
 __device__ __forceinline__ void pair_init(PairState<F, NT, CPL> &st, uint32_t lane,
-                                          uint32_t nbe, uint32_t stride, const int8_t *qs,
-                                          const uint16_t *d8, uint32_t K)
+                                          uint32_t nbe, uint32_t stride)
 {
     const uint32_t bx = lane < 32u ? 0u : stride, by = lane < 32u ? stride : 0u;
 #pragma unroll
@@ -649,10 +648,33 @@ __device__ __forceinline__ void pair_init(PairState<F, NT, CPL> &st, uint32_t la
         st.ox[i] = F::shifted(o, bx);
         if (i < CPL - 1)
             st.oy[i] = F::shifted(o, by);
+    }
+}
+
+// The lane's activation operands, with `between` (the first pairs' requests) issued
+// after their loads and before their arithmetic, as lane_acts_around.
+template <class F, int NT, int CPL, typename Between>
+__device__ __forceinline__ void pair_acts_around(PairState<F, NT, CPL> &st, const int8_t *qs,
+                                                 const uint16_t *d8, uint32_t K,
+                                                 Between &&between)
+{
+    ActRaw raw[CPL][NT];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-            st.act[i][t] = F::act(qs + (size_t)t * K, d8 + (size_t)t * (K / 32), Q);
+            raw[i][t] = F::act_raw(qs + (size_t)t * K, d8 + (size_t)t * (K / 32), st.Q[i]);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    between();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            st.act[i][t] = F::act_finish(raw[i][t]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // Pair p's loads: rows 2p and 2p + 1 below N under one descriptor (pairs past the
@@ -720,20 +742,32 @@ __global__ __launch_bounds__(WG) void mmvq_pairs(const uint8_t *__restrict__ w,
     const uint32_t wave = blockIdx.x * WAVES_PER_WG + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t nw = gridDim.x * WAVES_PER_WG;
     const uint32_t P = (N + 1u) / 2u;
-    PairState<F, NT, CPL> st;
-    pair_init(st, lane, nbe, stride, qs, d8, K);
     if (wave >= P)
         return;
+    PairState<F, NT, CPL> st;
+    pair_init(st, lane, nbe, stride);
     PairRing<F, CPL> b;
     uint32_t p = wave;
+    // the first pairs (DEPTH - 1, one at DEPTH 1) are requested right behind the
+    // operand loads and before the operand arithmetic, so the weight stream starts at
+    // once
+    pair_acts_around(st, qs, d8, K, [&] {
+        load_pair(b.A, w, p, N, stride, st);
+        if constexpr (DEPTH == 3) {
+            __builtin_amdgcn_sched_barrier(0);
+            load_pair(b.B, w, p + nw, N, stride, st);
+        }
+    });
     if constexpr (DEPTH == 1) {
-        for (; p < P; p += nw) {
+        for (;;) {
+            finish_pair<F, NT, CPL>(b.A, st, y, ldy, p, N, lane);
+            p += nw;
+            if (p >= P)
+                break;
             load_pair(b.A, w, p, N, stride, st);
             __builtin_amdgcn_sched_barrier(0);
-            finish_pair<F, NT, CPL>(b.A, st, y, ldy, p, N, lane);
         }
     } else if constexpr (DEPTH == 2) {
-        load_pair(b.A, w, p, N, stride, st);
         for (;;) {
             const uint32_t p1 = p + nw, p2 = p1 + nw;
             PAIR_STEP(B, p1, A, p);
@@ -745,8 +779,6 @@ __global__ __launch_bounds__(WG) void mmvq_pairs(const uint8_t *__restrict__ w,
             p = p2;
         }
     } else {
-        load_pair(b.A, w, p, N, stride, st);
-        load_pair(b.B, w, p + nw, N, stride, st);
         for (;;) {
             const uint32_t p1 = p + nw, p2 = p1 + nw, p3 = p2 + nw;
             PAIR_STEP(C, p2, A, p);
@@ -879,28 +911,32 @@ __global__ __launch_bounds__(WG) void gate_up_swiglu_rows(
     const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     LaneState<F, 1, CPL, ACT_REGS> st;
     lane_chunks(st, lane, nbe);
-    lane_acts(st, qs, d8, K);
     const uint32_t N = 2u * Nh, nblk = Nh / 32u;
+    // row i of this wave's 16 in block b (past the last block: N, an empty request)
+    auto block_row = [&](uint32_t b, uint32_t i) {
+        return b < nblk ? (i < 8u ? 0u : Nh) + 32u * b + 8u * wv + (i & 7u) : N;
+    };
     typename F::W A[CPL], B[CPL];
+    // the first row is requested right behind the operand loads and before their
+    // arithmetic; each block's last step requests the next block's first row
+    lane_acts_around(st, qs, d8, K,
+                     [&] { load_row(A, w, block_row(blockIdx.x, 0u), N, stride, st); });
     for (uint32_t b = blockIdx.x; b < nblk; b += gridDim.x) {
-        const uint32_t base = 32u * b + 8u * wv;
-        auto row_of = [&](uint32_t i) { return (i < 8u ? 0u : Nh) + base + (i & 7u); };
+        auto row_of = [&](uint32_t i) { return block_row(b, i); };
         auto take = [&](uint32_t i, float v) {
             if (lane == 0) {
                 gu[row_of(i)] = v;
                 (i < 8u ? s_g : s_u)[8u * wv + (i & 7u)] = v;
             }
         };
-        load_row(A, w, row_of(0), N, stride, st);
 #pragma unroll
         for (uint32_t i = 0; i < ROWS; i += 2) {
             load_row(B, w, row_of(i + 1), N, stride, st);
             __builtin_amdgcn_sched_barrier(0);
             take(i, row_total<F, 1, CPL, ACT_REGS>(A, st, nullptr, nullptr, K, lane));
-            if (i + 2 < ROWS) {
-                load_row(A, w, row_of(i + 2), N, stride, st);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            load_row(A, w, i + 2 < ROWS ? row_of(i + 2) : block_row(b + gridDim.x, 0u), N,
+                     stride, st);
+            __builtin_amdgcn_sched_barrier(0);
             take(i + 1, row_total<F, 1, CPL, ACT_REGS>(B, st, nullptr, nullptr, K, lane));
         }
         __syncthreads();
