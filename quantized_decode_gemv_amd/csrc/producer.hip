@@ -57,10 +57,15 @@ __global__ __launch_bounds__(QWG) void swiglu_quant_kernel(const float4 *g, cons
     }
 }
 
-// One workgroup of NORM_WG threads per token row, with the sum order of
-// q6k_norm.h. Rows of up to NORM_WG * VPT float4s keep their x and gamma in
-// registers; longer rows are read again after the sum. y is stored (when y is not
-// null) and quantized from registers, so the bytes equal quant_q8 applied to y.
+// Workgroups of NORM_WG threads, each computing a token row's whole sum in the order
+// of q6k_norm.h (so every workgroup of a row finds the same r) and then normalizing
+// and quantizing one group of it: workgroup (s, t) takes the float4s s * NORM_WG ..
+// s * NORM_WG + NORM_WG - 1 of token t, and the grid holds ceil(K / (4 * NORM_WG))
+// workgroups per token. One workgroup per token doing every group spent most of its
+// time on the q8 arithmetic of groups processed one after another on one CU. Rows of
+// up to NORM_WG * VPT float4s keep their x in registers; longer rows are read again
+// after the sum. y is stored (when y is not null) and quantized from registers, so
+// the bytes equal quant_q8 applied to y.
 template <int VPT>
 __global__ __launch_bounds__(NORM_WG) void rmsnorm_quant_regs(const float4 *__restrict__ x,
                                                               const float4 *__restrict__ g,
@@ -69,7 +74,8 @@ __global__ __launch_bounds__(NORM_WG) void rmsnorm_quant_regs(const float4 *__re
                                                               uint16_t *__restrict__ d8, uint32_t K)
 {
     __shared__ double part[NORM_WG / 64];
-    const uint32_t t = blockIdx.x;
+    const uint32_t t = blockIdx.y;
+    const int grp = (int)blockIdx.x;
     const uint32_t K4 = K / 4u;
     const __amdgpu_buffer_rsrc_t rx = buf_desc(x + (size_t)t * K4, 16u * K4),
                                  rg = buf_desc(g, 16u * K4);
@@ -83,15 +89,21 @@ __global__ __launch_bounds__(NORM_WG) void rmsnorm_quant_regs(const float4 *__re
     float4 *yr = y ? y + (size_t)t * K4 : nullptr;
     uint32_t *qr = qs + (size_t)t * K4;
     uint16_t *dr = d8 + (size_t)t * (K / 32u);
-    norm_quant_rows<1, VPT>(xv, gv, K, eps, part, [&](int, uint32_t f, float4 yv, const Q8Out &o) {
-        if (yr)
-            yr[f] = yv;
-        qr[f] = o.packed;
-        if ((f & 7u) == 0)
-            dr[f >> 3] = o.d16;
-    });
+    norm_quant_rows<1, VPT>(
+        xv, gv, K, eps, part,
+        [&](int, uint32_t f, float4 yv, const Q8Out &o) {
+            if (yr)
+                yr[f] = yv;
+            qr[f] = o.packed;
+            if ((f & 7u) == 0)
+                dr[f >> 3] = o.d16;
+        },
+        grp);
 }
 
+// Longer rows: every workgroup of a token sums the whole row (same order, same r),
+// then workgroup s normalizes and quantizes the passes s, s + S, ... of NORM_WG
+// float4s (S = gridDim.x workgroups per token).
 __global__ __launch_bounds__(NORM_WG) void rmsnorm_quant_loop(const float4 *__restrict__ x,
                                                               const float4 *__restrict__ g,
                                                               float eps, float4 *__restrict__ y,
@@ -99,7 +111,7 @@ __global__ __launch_bounds__(NORM_WG) void rmsnorm_quant_loop(const float4 *__re
                                                               uint16_t *__restrict__ d8, uint32_t K)
 {
     __shared__ double part[NORM_WG / 64];
-    const uint32_t t = blockIdx.x;
+    const uint32_t t = blockIdx.y;
     const uint32_t K4 = K / 4u;
     const float4 *xr = x + (size_t)t * K4;
     const uint32_t iters = (K4 + NORM_WG - 1) / NORM_WG;
@@ -113,7 +125,7 @@ __global__ __launch_bounds__(NORM_WG) void rmsnorm_quant_loop(const float4 *__re
     float4 *yr = y ? y + (size_t)t * K4 : nullptr;
     uint32_t *qr = qs + (size_t)t * K4;
     uint16_t *dr = d8 + (size_t)t * (K / 32u);
-    for (uint32_t it = 0; it < iters; ++it) {
+    for (uint32_t it = blockIdx.x; it < iters; it += gridDim.x) {
         const uint32_t f = it * NORM_WG + threadIdx.x;
         const bool live = f < K4;
         const float4 yv = live ? rms_scale(xr[f], g[f], r) : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -167,16 +179,22 @@ hipError_t launch_rmsnorm_quant(const float *x, const float *gamma, float eps, f
     void *args[] = {(void *)&x4, (void *)&g4, (void *)&eps, (void *)&y4,
                     (void *)&qs, (void *)&d8, (void *)&Ku};
     const int64_t K4 = K / 4;
+    // workgroups per token: one per group of NORM_WG float4s (the looping form: at
+    // most 16, each taking every 16th pass)
+    const uint32_t groups = (uint32_t)((K4 + NORM_WG - 1) / NORM_WG);
     const void *kern;
+    uint32_t per = groups;
     if (K4 <= NORM_WG * 2)
         kern = (const void *)rmsnorm_quant_regs<2>;
     else if (K4 <= NORM_WG * 4)
         kern = (const void *)rmsnorm_quant_regs<4>;
     else if (K4 <= NORM_WG * 8)
         kern = (const void *)rmsnorm_quant_regs<8>;
-    else
+    else {
         kern = (const void *)rmsnorm_quant_loop;
-    return hipLaunchKernel(kern, dim3(nt), dim3(NORM_WG), args, 0, s);
+        per = groups < 16u ? groups : 16u;
+    }
+    return hipLaunchKernel(kern, dim3(per, nt), dim3(NORM_WG), args, 0, s);
 }
 
 }  // namespace q6k

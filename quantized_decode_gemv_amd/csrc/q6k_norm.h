@@ -181,12 +181,14 @@ __device__ __forceinline__ float4 rms_scale(float4 x, float4 g, float r)
 // RMSNorm -> q8 of NT token rows held in registers by a NORM_WG-thread workgroup:
 // xv[t][v] and gv[v] are the float4s threadIdx.x + v * NORM_WG of token t's x and of
 // gamma (zeros past K/4). Calls put(t, f, y, q8) for every live float4 index f
-// (q8.d16 is the scale of block f / 8). Every thread must call it; part holds
+// (q8.d16 is the scale of block f / 8) of group `only` (v == only; every group when
+// only < 0; only is the same for the whole workgroup). The sum always covers every
+// group, so r does not depend on `only`. Every thread must call it; part holds
 // NORM_WG / 64 doubles of LDS per token.
 template <int NT, int VPT, bool SKIP_PAST = false, typename Put>
 __device__ __forceinline__ void norm_quant_rows(const float4 (&xv)[NT][VPT],
                                                 const float4 (&gv)[VPT], uint32_t K, float eps,
-                                                double *part, Put &&put)
+                                                double *part, Put &&put, int only = -1)
 {
     const uint32_t K4 = K / 4u;
 #pragma unroll
@@ -204,6 +206,8 @@ __device__ __forceinline__ void norm_quant_rows(const float4 (&xv)[NT][VPT],
         for (int v = 0; v < VPT; ++v) {
             if (SKIP_PAST && (uint32_t)v * NORM_WG >= K4)
                 break;
+            if (only >= 0 && v != only)
+                continue;
             const uint32_t f = threadIdx.x + v * NORM_WG;
             const float4 yv = rms_scale(xv[t][v], gv[v], r);
             const Q8Out o = quant_group8(yv);
