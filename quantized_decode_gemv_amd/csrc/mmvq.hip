@@ -509,18 +509,17 @@ __global__ __launch_bounds__(WG) void mmvq_rows(const uint8_t *__restrict__ w,
         if (wave >= N)
             return;
     } else {
-        // the activation operands first: with the weight rows requested before them,
-        // waiting for the operands (issued later) waits for the rows too, and the
-        // compiler's wait counts at the row loop's head then cover the look-ahead rows
-        // as well (measured slower on every shape it changed)
+        // Order of the start: the activation operands' loads, then the first rows'
+        // requests (one row with DEPTH 1, which then walks primed; DEPTH - 1
+        // otherwise), then the operand arithmetic, which waits for the operand loads
+        // only. Rows requested before the operand loads made that wait cover the rows
+        // too, and the compiler's wait counts at the row loop's head then covered the
+        // look-ahead rows as well (measured slower on every shape it changed); rows
+        // requested after the operand arithmetic started a wave's weight stream up to
+        // about 1 us late (per-wave clock stamps, 5120 x 13824 at one token).
         lane_chunks(st, lane, nbe);
         if (wave >= N)
             return;
-        // the first rows are requested right behind the operand loads and before
-        // their arithmetic, so the weight stream starts at once: one row with DEPTH 1
-        // (which then walks primed), DEPTH - 1 otherwise. With requests after the
-        // operand arithmetic, which waits for the operand loads, a wave's stream started
-        // up to about 1 us late (per-wave clock stamps, 5120 x 13824 at one token).
         auto first_rows = [&] {
             prime_rows<F, NT, CPL, 0, DEPTH == 1 ? 1 : DEPTH - 1, AM>(bufs, w, wave, nw, N,
                                                                      stride, st);
