@@ -26,12 +26,17 @@
 // bytes measured markedly slower, as the row stride is not a multiple of the 128-byte
 // line) into one of two tile buffers, while they compute the other. Wave v computes
 // super-blocks 5v .. 5v + 4 of all 16 rows; the four partial sums of a row meet in
-// LDS and wave t adds them for token t and stores y. Its activation operands (A, C
-// and the q8 block scales, as fp16 pairs) depend only on the wave's K quarter, so they
-// are loaded once and stay in registers for every tile (251 registers at 4 tokens; C
+// LDS, and wave t adds them for token t and stores y after a later tile's landing
+// (every tile at 4 tokens, every fourth at 3). Its activation operands (A, C and the
+// q8 block scales, as fp16 pairs) depend only on the wave's K quarter, so they are
+// loaded once and stay in registers for every tile (about 256 registers at 4 tokens; C
 // read from an LDS table per step instead measured about 4 us slower). Per tile: two
 // barriers (buffer free; tile landed), each wave's own copies awaited with a counted
-// wait (vm_wait), as the compiler does not count buffer-to-LDS loads.
+// wait (vm_wait), as the compiler does not count buffer-to-LDS loads. An output store
+// made after tile s - 1's landing lies between the copies of tile s and those of tile
+// s + 1 in issue order; loads complete in issue order, so while a copy of tile s is
+// outstanding all RUNS copies of tile s + 1 are too, and a count of at most RUNS
+// still means that tile s has landed, whenever the store completes.
 //
 // What bounds it: two 66 KB tile buffers are what LDS holds, so a CU has at most one
 // tile in flight, and none between the landing of one tile's copies and the issue of
@@ -109,7 +114,13 @@ __global__ __launch_bounds__(256) void mmvq_tiles(const uint8_t *__restrict__ w,
     constexpr uint32_t SPW = TG::SPW;
     constexpr uint32_t K = 256u * NBE;
     __shared__ __align__(16) uint8_t tbuf[2 * TG::BUF];
-    __shared__ float part[2][WAVES][4][TILE_ROWS];
+    // tiles per output store (see store_tiles), and the partial sums of the last PSLOTS
+    // tiles: [tile % PSLOTS][wave][token][row]. At 3 tokens one store per four tiles
+    // measured up to 1 us faster than one per tile; at 4 tokens, where the loop holds
+    // about 256 registers, the wider store path measured 2 us slower.
+    constexpr uint32_t PER = NT == 4 ? 1u : 4u;
+    constexpr uint32_t PSLOTS = 2u * PER;
+    __shared__ float part[PSLOTS][WAVES][4][TILE_ROWS];
 
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // K quarter
@@ -124,10 +135,16 @@ __global__ __launch_bounds__(256) void mmvq_tiles(const uint8_t *__restrict__ w,
     const uint32_t rest = N - rows_full;
     const uint32_t share = (rest + NG - 1u) / NG;
     const uint32_t S = FR + (rest ? 1u : 0u);
+    // the workgroup's place in a round of whole tiles: workgroup b runs on XCD b % 8, and
+    // the two tiles whose outputs share a 128-byte line of y (16 rows x 4 bytes each, per
+    // token) go to two workgroups of one XCD, so that the line is written through one L2
+    // (pieces of a line written back from several L2s measured slower)
+    const uint32_t bx = blockIdx.x;
+    const uint32_t place = NG % 16u == 0 ? (bx & ~15u) + 2u * (bx & 7u) + ((bx >> 3) & 1u) : bx;
     // first row and rows of tile s (none past the last)
     auto tile_rows = [&](uint32_t s, uint32_t &r0) -> uint32_t {
         if (s < FR) {
-            r0 = (blockIdx.x + s * NG) * TILE_ROWS;
+            r0 = (place + s * NG) * TILE_ROWS;
             return TILE_ROWS;
         }
         r0 = rows_full + blockIdx.x * share;
@@ -148,17 +165,27 @@ __global__ __launch_bounds__(256) void mmvq_tiles(const uint8_t *__restrict__ w,
             dma_b128(rs, 16u * lane, 1024u * run, lds0 + b * TG::BUF + 1024u * run);
         }
     };
-    // wave t (a token) stores tile s's outputs for token t: the waves' partial sums of
-    // row `lane`, added in wave order
-    auto store_tile = [&](uint32_t s, const float (&pp)[WAVES][4][TILE_ROWS]) {
-        uint32_t r0;
-        const uint32_t rows = tile_rows(s, r0);
-        if (lane < rows) {
-            float tot = pp[0][wv][lane];
+    // wave t (a token) stores token t's outputs of tiles j0 .. j0 + PER - 1 (those below
+    // S) in one store: lane l takes row l % 16 of tile j0 + l / 16, the sum of the waves'
+    // partial sums of that row, added in wave order
+    auto store_tiles = [&](uint32_t j0) {
+        uint32_t r0 = 0, rows, j, rr;
+        if constexpr (PER == 1) {
+            j = j0;
+            rr = lane;
+            rows = tile_rows(j0, r0);
+        } else {
+            j = j0 + (lane >> 4u);
+            rr = lane & 15u;
+            rows = (lane >> 4u) < PER && j < S ? tile_rows(j, r0) : 0u;
+        }
+        if (rr < rows) {
+            const uint32_t sl = j % PSLOTS;
+            float tot = part[sl][0][wv][rr];
 #pragma unroll
             for (int u = 1; u < WAVES; ++u)
-                tot += pp[u][wv][lane];
-            y[(size_t)wv * ldy + r0 + lane] = tot;
+                tot += part[sl][u][wv][rr];
+            y[(size_t)wv * ldy + r0 + rr] = tot;
         }
     };
 
@@ -217,8 +244,8 @@ __global__ __launch_bounds__(256) void mmvq_tiles(const uint8_t *__restrict__ w,
         copy_tile(b ^ 1u, s + 1u);
         vm_wait<(int)TG::RUNS>();   // this wave's copies of tile s have landed
         __syncthreads();            // and every wave's
-        if (s > 0 && wv < (uint32_t)NT)
-            store_tile(s - 1u, part[b ^ 1u]);
+        if (s % PER == 0 && s > 0 && wv < (uint32_t)NT)
+            store_tiles(s - PER);
         const uint8_t *rb = tbuf + b * TG::BUF + r * TG::STRIDE;
         float acc[NT];
 #pragma unroll
@@ -273,11 +300,11 @@ __global__ __launch_bounds__(256) void mmvq_tiles(const uint8_t *__restrict__ w,
             x += __shfl_xor(x, 16);
             mine = g == (uint32_t)t ? x : mine;
         }
-        part[b][wv][g][r] = mine;
+        part[s % PSLOTS][wv][g][r] = mine;
     }
     __syncthreads();
     if (wv < (uint32_t)NT)
-        store_tile(S - 1u, part[(S - 1u) & 1u]);
+        store_tiles((S - 1u) / PER * PER);
     // no copy may still be landing in LDS when the workgroup ends
     vm_wait<0>();
 }
