@@ -93,6 +93,30 @@ __device__ __forceinline__ uint32_t lds_offset(const void *p)
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t *)p;
 }
 
+// x + (x of lane l ^ 32), and x + (x of lane l ^ 16): the values and the order of
+// x + __shfl_xor(x, 32 or 16), with the lanes exchanged in the vector ALU
+// (v_permlane32_swap / v_permlane16_swap) instead of by a permute through LDS, whose
+// round trip sat in every tile's reduction. With both operands x, the 32-lane swap
+// returns (x of lane l - 32 in the upper half) and (x of lane l + 32 in the lower
+// half); the 16-lane swap does the same for the odd and even 16-lane rows. (The two
+// results are copied into plain integers before their bit casts: a bit cast applied
+// straight to an element of the returned pair reads element 0 for both.)
+__device__ __forceinline__ float add_xor32(float x, uint32_t lane)
+{
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const unsigned h0 = h[0], h1 = h[1];
+    return x + __builtin_bit_cast(float, lane < 32u ? h1 : h0);
+}
+
+__device__ __forceinline__ float add_xor16(float x, uint32_t lane)
+{
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto h = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const unsigned h0 = h[0], h1 = h[1];
+    return x + __builtin_bit_cast(float, (lane & 16u) ? h0 : h1);
+}
+
 __device__ __forceinline__ i32x4 as_i32x4(uint4 v)
 {
     i32x4 r;
@@ -194,6 +218,8 @@ __global__ __launch_bounds__(256) void mmvq_tiles(const uint8_t *__restrict__ w,
     // first tile's copies, as a wave's loads complete in issue order and would otherwise
     // wait behind them. The scales come as one 16-byte load per token and super-block.
     i32x4 A[4 * SPW], C[4 * SPW];
+    const i32x4 NEG32 = {(int)0xE0E0E0E0u, (int)0xE0E0E0E0u, (int)0xE0E0E0E0u, (int)0xE0E0E0E0u};
+    const i32x4 ZERO4 = {0, 0, 0, 0};
     uint32_t Fh[2 * SPW][2];
     {
         const uint32_t ia = lane & 15u, ta = ia & 3u, sa = ia >> 2;
@@ -208,12 +234,11 @@ __global__ __launch_bounds__(256) void mmvq_tiles(const uint8_t *__restrict__ w,
                 const uint32_t off = 256u * sb + 128u * c + 32u * a + 64u * (j >> 1) + 16u * (j & 1u);
                 const uint4 x = load_b128<POLICY_DEFAULT>(xr, xbase + (live ? off : 0u));
                 A[4 * m + j] = as_i32x4(x);
-                const int ns = -32 * sum16_i8(x);
-                // lane (r, g) takes, for token t, the sum of A row 4g + t in K-group g:
-                // lane 16g + 4g + t
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    C[4 * m + j][t] = __builtin_amdgcn_ds_bpermute((int)(4u * (20u * g + t)), ns);
+                // C = A times a B of all -32: every column holds -32 * (the sum of each A
+                // row), and lane (r, g) receives rows 4g .. 4g + 3, the four tokens' sums
+                // of slot g, in the layout the step's own product adds them to (exact:
+                // at most 16 * 128 * 32 in magnitude)
+                C[4 * m + j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[4 * m + j], NEG32, ZERO4, 0, 0, 0);
             }
             // the super-block's 8 q8 block scales of each token (16 bytes), of which
             // blocks 4c + a and 4c + a + 2 are this lane's
@@ -296,8 +321,8 @@ __global__ __launch_bounds__(256) void mmvq_tiles(const uint8_t *__restrict__ w,
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             float x = acc[t];
-            x += __shfl_xor(x, 32);
-            x += __shfl_xor(x, 16);
+            x = add_xor32(x, lane);
+            x = add_xor16(x, lane);
             mine = g == (uint32_t)t ? x : mine;
         }
         part[s % PSLOTS][wv][g][r] = mine;
