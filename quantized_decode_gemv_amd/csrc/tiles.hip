@@ -140,8 +140,8 @@ __global__ __launch_bounds__(256) void mmvq_tiles(const uint8_t *__restrict__ w,
     __shared__ __align__(16) uint8_t tbuf[2 * TG::BUF];
     // tiles per output store (see store_tiles), and the partial sums of the last PSLOTS
     // tiles: [tile % PSLOTS][wave][token][row]. At 3 tokens one store per four tiles
-    // measured up to 1 us faster than one per tile; at 4 tokens, where the loop holds
-    // about 256 registers, the wider store path measured 2 us slower.
+    // measured 0.1-0.8 us faster than one per tile; at 4 tokens, where the loop holds
+    // about 256 registers, the wider store path measured 2-3 us slower.
     constexpr uint32_t PER = NT == 4 ? 1u : 4u;
     constexpr uint32_t PSLOTS = 2u * PER;
     __shared__ float part[PSLOTS][WAVES][4][TILE_ROWS];
