@@ -68,6 +68,7 @@ __device__ __forceinline__ uint32_t wg_place()
     const uint32_t b = blockIdx.x;
     return gridDim.x % 64u == 0 ? (b & ~63u) + 8u * (b & 7u) + ((b >> 3) & 7u) : b;
 }
+
 constexpr int MAX_CPL = 12;         // nbe <= 96 take the fixed-length kernels
 constexpr int MAX_NT_KERNEL = 4;    // token columns per launch (more -> several launches)
 
