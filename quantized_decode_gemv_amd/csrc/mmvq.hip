@@ -1549,12 +1549,17 @@ hipError_t launch_fused_fmt(const uint8_t *w, const float *x, const float *gamma
     a.stride = (uint32_t)kq_row_stride(F::TYPE, nbe);
     a.K = (uint32_t)K;
     a.ldy = (uint32_t)N;
-    // q6_K rows of three chunks per lane: two workgroups per CU, where the GEMV alone keeps
-    // one. The norm phase runs at one wave per SIMD, bound by its dependent arithmetic;
-    // with two workgroups per CU it runs at two, half the rows per wave (same bits out;
-    // K = 5120 at one token: 152064 rows 90.26 -> 90.03 us, 65536 rows 41.69 -> 40.38,
-    // where the GEMV alone at two ran 88.30 -> 89.53 and 39.76 -> 39.81)
-    const int wpc = (F::TYPE == KQT_Q6_K && cpl == 3) ? 2 : c.wg_per_cu;
+    // q6_K rows of three to six chunks per lane: two workgroups per CU, where the GEMV
+    // alone keeps one. The norm phase runs at one wave per SIMD, bound by its dependent
+    // arithmetic; with two workgroups per CU it runs at two, half the rows per wave (same
+    // bits out; one token, K = 5120: 152064 rows 90.26 -> 90.03 us, 65536 rows 41.69 ->
+    // 40.38, where the GEMV alone at two ran 88.30 -> 89.53 and 39.76 -> 39.81; 32768
+    // rows at K = 8192 35.31 -> 33.42, 10240 43.60 -> 41.45, 12288 51.54 -> 50.01). Only
+    // from four rows per wave at two workgroups per CU: every workgroup redoes the norm,
+    // and 4096 rows at K = 10240 (two rows per wave) measured 10.86 -> 12.28.
+    const bool two = F::TYPE == KQT_Q6_K && cpl >= 3 && cpl <= 6 &&
+                     N >= (int64_t)4 * 2 * WAVES_PER_WG * num_cu;
+    const int wpc = two ? 2 : c.wg_per_cu;
     return dispatch_fused<F, 1>(cpl, c.depth, std::make_integer_sequence<int, FUSED_MAX_CPL>{},
                                 num_cu, wpc, s, a);
 }
